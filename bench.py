@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Throughput of the fused chunked KL loss (forward + backward) on one MI355X.
+
+One step = one ckl_fwd_bwd call over the whole batch: every chunk's logits
+GEMM, row pass (log-normaliser, gather, KL, in-place gradient), dH and dW
+GEMMs, with inputs already resident in HBM.  Default workload: the
+gpt-oss-like head, N = 32,768 tokens (1 x 32K), d = 2880, V = 201,088, K = 100,
+chunk chosen by the planner under the 6 GiB workspace budget.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+GEMM_SOURCES = ["chunked_kl_loss_seq_amd/csrc/gemm_core.hpp", "chunked_kl_loss_seq_amd/csrc/kernels_gemm.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_kind):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current GEMM sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_kind}_gemm_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_sha") != source_hash(GEMM_SOURCES):
+            return None
+        return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(number, rows):
+    """The oracle as it stands, timed on the host cores over a bounded sample."""
+    import numpy as np  # noqa: F401
+
+    from chunked_kl_loss_seq_amd import workloads as WL
+    from oracle import kl_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = WL.make(number, rows=rows)
+    t0 = time.perf_counter()
+    O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
+    dt = time.perf_counter() - t0
+    valid = int(inp["mask"].sum())
+    return {"value": valid / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} positions of the same workload, float64 NumPy/BLAS dense definition, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4, help="named workload number (4 = gpt-oss head, 32K tokens)")
+    ap.add_argument("--chunk", type=int, default=-1, help="rows per chunk (default: the workload's own)")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="positions in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from chunked_kl_loss_seq_amd import binding
+    from chunked_kl_loss_seq_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    binding.lib()
+    wl = WL.WORKLOADS[args.workload]
+    chunk = wl.chunk if args.chunk < 0 else args.chunk
+    log(f"[bench] generating {wl.name}: N={wl.N} d={wl.d} V={wl.V} K={wl.K}")
+    inp = WL.make(args.workload)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    H = torch.from_numpy(inp["H"]).to(dev).to(tdt)
+    W = torch.from_numpy(inp["W"]).to(dev).to(tdt)
+    ids = torch.from_numpy(inp["ids"]).to(dev)
+    T = torch.from_numpy(inp["tlogit"]).to(dev)
+    mask = torch.from_numpy(inp["mask"]).to(dev) if wl.mask != "none" else None
+    n_valid = int(inp["mask"].sum())
+    N, d, V, K = wl.N, wl.d, wl.V, wl.K
+    C, ws_plan = binding.plan(N, d, V, K, wl.dtype, chunk)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    del inp["H"], inp["W"]
+
+    log(f"[bench] chunk {C} rows, planned workspace {ws_plan / 2**30:.3f} GiB; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        binding.fwd_bwd(H, W, ids, T, mask, chunk, out_loss=loss, dH=dH, dW=dW)
+    torch.cuda.synchronize()
+    log(f"[bench] warm, loss {loss.item():.6f}; timing {args.steps} steps")
+
+    binding.timing_enable(True)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        binding.fwd_bwd(H, W, ids, T, mask, chunk, out_loss=loss, dH=dH, dW=dW)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kinds = {}
+    for k in ("logits", "rows", "dh", "dh_reduce", "dw", "other"):
+        t, n = binding.timing_query(k)
+        kinds[k] = (t, n)
+    binding.timing_enable(False)
+    ws_held = binding.workspace_bytes_held()
+
+    flop_gemm_launch_total = 2.0 * n_valid * d * V * args.steps  # per GEMM kind over the timed region
+    gemm = {k: kinds[k] for k in ("logits", "dh", "dw")}
+    dom = max(gemm, key=lambda k: gemm[k][0])
+    dom_ms, dom_n = gemm[dom]
+    achieved = flop_gemm_launch_total / (dom_ms / 1e3) / 1e12
+    total_tflops = 6.0 * n_valid * d * V / (ms / 1e3) / 1e12
+    peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
+    per_kernel = {k: {"ms_per_step": kinds[k][0] / args.steps, "launches_per_step": kinds[k][1] / args.steps}
+                  for k in kinds}
+    for k in ("logits", "dh", "dw"):
+        per_kernel[k]["tflops"] = flop_gemm_launch_total / (kinds[k][0] / 1e3) / 1e12 if kinds[k][0] else None
+    traffic = traffic_from_profile(dom)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": f"{dom} GEMM",
+                "launch_avg_ms": round(dom_ms / max(dom_n, 1), 4)}
+    log(f"[bench] {ms:.2f} ms/step, {N / (ms / 1e3):.0f} tokens/s, {total_tflops:.1f} TFLOP/s whole step")
+    for k, v in per_kernel.items():
+        log(f"[bench]   {k:10s} {v['ms_per_step']:8.3f} ms/step  launches {v['launches_per_step']:.0f}"
+            + (f"  {v['tflops']:.1f} TFLOP/s" if v.get("tflops") else ""))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the oracle on {args.cpu_rows} positions")
+        cpu = cpu_baseline(args.workload, args.cpu_rows)
+        log(f"[bench] oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": "fused KL fwd+bwd tokens/s + MFMA TFLOP/s % peak; peak workspace GiB",
+        "value": round(N / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "N": N, "valid_tokens": n_valid, "d": d, "V": V, "K": K, "chunk": C,
+                   "global_batch": N // (wl.seq_len or N), "seq_len": wl.seq_len or N, "parallelism": "none"},
+        "tokens_per_s_valid": round(n_valid / (ms / 1e3), 1),
+        "tflops": round(total_tflops, 2),
+        "pct_bf16_peak": round(100 * total_tflops / BF16_PEAK_TFLOPS, 2),
+        "workspace_gib": round(ws_plan / 2**30, 4),
+        "workspace_held_gib": round(ws_held / 2**30, 4),
+        "per_kernel": per_kernel,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,16 @@
+"""Fused chunked KL distillation loss for MI355X (gfx950): HIP kernels behind a C ABI.
+
+``binding`` loads libckl.so on first use and raises if it is missing;
+``workloads`` draws the seeded synthetic inputs.
+"""
+from .binding import (  # noqa: F401
+    CklError,
+    debug_rows,
+    fused_kl,
+    fwd_bwd,
+    plan,
+    release_workspace,
+    timing_enable,
+    timing_query,
+    workspace_bytes_held,
+)

@@ -1,0 +1,205 @@
+"""Thin ctypes binding of libckl.so (argument marshalling only).
+
+Every step of the loss runs in the library's HIP kernels; PyTorch only
+supplies device memory and the current stream.  There is no fallback: if the
+library is missing, or the tensors are not on a GPU, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libckl.so")
+
+CKL_OK = 0
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+TIMING_KINDS = {"logits": 0, "rows": 1, "dh": 2, "dh_reduce": 3, "dw": 4, "other": 5}
+
+_lib = None
+
+
+class CklError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+
+
+def lib():
+    """Load libckl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m chunked_kl_loss_seq_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, u64, vp, f32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_float
+    L.ckl_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp]
+    L.ckl_fwd_bwd.restype = ctypes.c_int
+    L.ckl_fwd_bwd_f32.argtypes = L.ckl_fwd_bwd.argtypes
+    L.ckl_fwd_bwd_f32.restype = ctypes.c_int
+    L.ckl_fwd_bwd_ex.argtypes = [ctypes.c_int] + L.ckl_fwd_bwd.argtypes[:-1] + [vp, vp, vp]
+    L.ckl_fwd_bwd_ex.restype = ctypes.c_int
+    L.ckl_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, i64, u64, ctypes.POINTER(i64), ctypes.POINTER(u64)]
+    L.ckl_plan.restype = ctypes.c_int
+    L.ckl_release_workspace.argtypes = []
+    L.ckl_release_workspace.restype = None
+    L.ckl_workspace_bytes_held.argtypes = []
+    L.ckl_workspace_bytes_held.restype = u64
+    L.ckl_strerror.argtypes = [ctypes.c_int]
+    L.ckl_strerror.restype = ctypes.c_char_p
+    L.ckl_debug_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    L.ckl_debug_rows.restype = ctypes.c_int
+    L.ckl_timing_enable.argtypes = [ctypes.c_int]
+    L.ckl_timing_enable.restype = ctypes.c_int
+    L.ckl_timing_query.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    L.ckl_timing_query.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def strerror(status):
+    return lib().ckl_strerror(int(status)).decode()
+
+
+def _check(st, what):
+    if st != CKL_OK:
+        raise CklError(st, what)
+
+
+def plan(N, d, V, K, dtype="bf16", chunk=0, budget_bytes=0):
+    """(chunk rows, workspace bytes) the library will use for this shape."""
+    c = ctypes.c_int64(0)
+    b = ctypes.c_uint64(0)
+    dt = DTYPE_BF16 if dtype == "bf16" else DTYPE_F32
+    _check(lib().ckl_plan(N, d, V, K, dt, chunk, budget_bytes, ctypes.byref(c), ctypes.byref(b)), "ckl_plan")
+    return int(c.value), int(b.value)
+
+
+def release_workspace():
+    lib().ckl_release_workspace()
+
+
+def workspace_bytes_held():
+    return int(lib().ckl_workspace_bytes_held())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=None, row_kl=None,
+            row_lse=None):
+    """Loss, dH and dW of the fused chunked KL loss; tensors on one GPU.
+
+    H [N,d] and W [V,d] are both bfloat16 or both float32; ids int32 [N,K];
+    tlogit float32 [N,K]; mask uint8/bool [N] or None.  Returns
+    (loss 0-dim float32, dH like H, dW float32 [V,d]), all enqueued on the
+    current stream.  ``row_kl`` / ``row_lse`` (float32 [N] tensors) receive
+    the per-position KL and student logsumexp when given.
+    """
+    import torch
+
+    if not H.is_cuda:
+        raise ValueError("fwd_bwd needs GPU tensors")
+    N, d = H.shape
+    V = W.shape[0]
+    K = ids.shape[1]
+    for name, t in (("H", H), ("W", W), ("ids", ids), ("tlogit", tlogit)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if ids.dtype != torch.int32 or tlogit.dtype != torch.float32:
+        raise ValueError("ids must be int32 and tlogit float32")
+    if H.dtype != W.dtype or H.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("H and W must both be bfloat16 or both float32")
+    if mask is not None:
+        mask = mask.to(torch.uint8).contiguous()
+    dev = H.device
+    if out_loss is None:
+        out_loss = torch.empty((), dtype=torch.float32, device=dev)
+    if dH is None:
+        dH = torch.empty_like(H)
+    if dW is None:
+        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    st_dev = _stream(torch, dev)
+    if row_kl is None and row_lse is None:
+        fn = lib().ckl_fwd_bwd if H.dtype == torch.bfloat16 else lib().ckl_fwd_bwd_f32
+        st = fn(_ptr(H), _ptr(W), _ptr(ids), _ptr(tlogit), _ptr(mask), N, d, V, K, int(chunk),
+                _ptr(out_loss), _ptr(dH), _ptr(dW), st_dev)
+    else:
+        dt = DTYPE_BF16 if H.dtype == torch.bfloat16 else DTYPE_F32
+        st = lib().ckl_fwd_bwd_ex(dt, _ptr(H), _ptr(W), _ptr(ids), _ptr(tlogit), _ptr(mask), N, d, V, K,
+                                  int(chunk), _ptr(out_loss), _ptr(dH), _ptr(dW), _ptr(row_kl), _ptr(row_lse),
+                                  st_dev)
+    _check(st, "ckl_fwd_bwd")
+    return out_loss, dH, dW
+
+
+def debug_rows(Z, ids, tlogit, mask=None, scale=1.0, g_bf16=True):
+    """Row pass alone on caller-given fp32 logits Z [R,V] (synchronises)."""
+    import torch
+
+    R, V = Z.shape
+    K = ids.shape[1]
+    dev = Z.device
+    zg = torch.empty((R, K), dtype=torch.float32, device=dev)
+    sid = torch.empty((R, K), dtype=torch.int32, device=dev)
+    G = torch.empty((R, V), dtype=torch.bfloat16 if g_bf16 else torch.float32, device=dev)
+    kl = torch.empty((R,), dtype=torch.float32, device=dev)
+    lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    if mask is not None:
+        mask = mask.to(torch.uint8).contiguous()
+    st = lib().ckl_debug_rows(_ptr(Z.contiguous()), _ptr(ids), _ptr(tlogit), _ptr(mask), R, V, K,
+                              float(scale), 1 if g_bf16 else 0, _ptr(zg), _ptr(sid), _ptr(G), _ptr(kl),
+                              _ptr(lse), _stream(torch, dev))
+    _check(st, "ckl_debug_rows")
+    return {"zg": zg, "sid": sid, "G": G, "kl": kl, "lse": lse}
+
+
+def timing_enable(on=True):
+    _check(lib().ckl_timing_enable(1 if on else 0), "ckl_timing_enable")
+
+
+def timing_query(kind):
+    """(total milliseconds, launches) recorded for one kernel kind since enabling."""
+    t = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    _check(lib().ckl_timing_query(TIMING_KINDS[kind], ctypes.byref(t), ctypes.byref(n)), "ckl_timing_query")
+    return float(t.value), int(n.value)
+
+
+class _FusedKL:
+    """torch.autograd.Function wrapper, created lazily so importing needs no torch."""
+
+    _fn = None
+
+    @classmethod
+    def get(cls):
+        if cls._fn is None:
+            import torch
+
+            class FusedKL(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, H, W, ids, tlogit, mask, chunk):
+                    loss, dH, dW = fwd_bwd(H.contiguous(), W.contiguous(), ids, tlogit, mask, chunk)
+                    ctx.save_for_backward(dH, dW)
+                    ctx.w_dtype = W.dtype
+                    return loss
+
+                @staticmethod
+                def backward(ctx, g):
+                    dH, dW = ctx.saved_tensors
+                    return (g * dH).to(dH.dtype), (g * dW).to(ctx.w_dtype), None, None, None, None
+
+            cls._fn = FusedKL
+        return cls._fn
+
+
+def fused_kl(H, W, ids, tlogit, mask=None, chunk=0):
+    """Loss as a differentiable torch scalar: gradients were computed in the forward pass."""
+    return _FusedKL.get().apply(H, W, ids, tlogit, mask, chunk)

@@ -1,0 +1,424 @@
+// C ABI of the fused chunked KL loss: argument checks, chunk planner,
+// workspace cache and the chunk loop that enqueues the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "../../include/ckl.h"
+#include "launch.hpp"
+
+using namespace ckl;
+
+namespace {
+
+constexpr uint64_t kDefaultBudget = 6ull << 30;
+constexpr int64_t kRowStep = 256;
+
+inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+inline int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Device workspace of one call with chunks of C rows.
+struct Layout {
+  int64_t C = 0;
+  int64_t ldz = 0;      // fp32 elements per logit row
+  int n_slices = 0;     // (max, sum exp) pairs per row
+  int splits = 0;       // k-splits of the dH contraction
+  uint64_t z_off = 0, part_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0, total = 0;
+};
+
+Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t C) {
+  Layout L;
+  L.C = C;
+  L.ldz = roundup(V, 64);
+  L.n_slices = (int)((V + 127) / 128);
+  L.splits = dh_splits(C, d, V);
+  uint64_t off = 0;
+  L.z_off = off;
+  off += align256((uint64_t)C * L.ldz * 4);
+  L.part_off = off;
+  off += align256((uint64_t)C * L.n_slices * 8);
+  L.slab_off = off;
+  off += align256((uint64_t)L.splits * C * d * 4);
+  L.kl_off = off;
+  off += align256((uint64_t)N * 4);
+  L.lse_off = off;
+  off += align256((uint64_t)N * 4);
+  L.scal_off = off;
+  off += 256;
+  L.total = off;
+  return L;
+}
+
+uint64_t budget_from_env(uint64_t b) {
+  if (b) return b;
+  const char* e = std::getenv("CKL_WORKSPACE_BYTES");
+  if (e && *e) {
+    char* end = nullptr;
+    unsigned long long v = std::strtoull(e, &end, 10);
+    if (end != e && v > 0) return (uint64_t)v;
+  }
+  return kDefaultBudget;
+}
+
+int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_t budget, Layout* out) {
+  if (N <= 0 || d <= 0 || V <= 0 || K <= 0 || chunk < 0) return CKL_EINVAL;
+  if (K > V) return CKL_EINVAL;
+  if (d % 8 != 0 || K > kMaxK) return CKL_EUNSUPPORTED;
+  if (V > (int64_t)1 << 30 || N > (int64_t)1 << 31 || d > (int64_t)1 << 20) return CKL_EUNSUPPORTED;
+  budget = budget_from_env(budget);
+  if (chunk > 0) {
+    const int64_t C = chunk < N ? chunk : N;
+    Layout L = make_layout(N, d, V, C);
+    if (L.total > budget) return CKL_EBUDGET;
+    *out = L;
+    return CKL_OK;
+  }
+  // largest fitting multiple of 256 rows (or N itself when smaller)
+  int64_t cmax = 0;
+  if (N <= kRowStep) {
+    if (make_layout(N, d, V, N).total <= budget) cmax = N;
+  } else {
+    int64_t lo = 1, hi = roundup(N, kRowStep) / kRowStep;  // in units of 256 rows
+    if (make_layout(N, d, V, kRowStep).total > budget) return CKL_EBUDGET;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (make_layout(N, d, V, mid * kRowStep).total <= budget)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    cmax = lo * kRowStep;
+    if (cmax > N) cmax = N;
+  }
+  if (cmax == 0) return CKL_EBUDGET;
+  // even out: same number of chunks, the smallest 256-multiple that covers N
+  const int64_t nch = (N + cmax - 1) / cmax;
+  int64_t C = roundup((N + nch - 1) / nch, kRowStep);
+  if (C > cmax) C = cmax;
+  if (C > N) C = N;
+  *out = make_layout(N, d, V, C);
+  return CKL_OK;
+}
+
+// ------------------------------------------------------------------ workspace cache
+struct WsKey {
+  int dev;
+  hipStream_t stream;
+  bool operator<(const WsKey& o) const { return dev != o.dev ? dev < o.dev : stream < o.stream; }
+};
+struct WsBuf {
+  void* ptr = nullptr;
+  uint64_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<WsKey, WsBuf> g_ws;
+
+int get_workspace(int dev, hipStream_t s, uint64_t bytes, void** ptr) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  WsBuf& b = g_ws[WsKey{dev, s}];
+  if (b.bytes >= bytes) {
+    *ptr = b.ptr;
+    return CKL_OK;
+  }
+  if (b.ptr) {
+    // the previous call on this stream may still be using the old buffer
+    if (hipStreamSynchronize(s) != hipSuccess) return CKL_EHIP;
+    if (hipFree(b.ptr) != hipSuccess) return CKL_EHIP;
+    b.ptr = nullptr;
+    b.bytes = 0;
+  }
+  const char* fail = std::getenv("CKL_TEST_FAIL_ALLOC");
+  if (fail && fail[0] == '1') return CKL_ENOMEM;
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return CKL_ENOMEM;
+  }
+  b.ptr = p;
+  b.bytes = bytes;
+  *ptr = p;
+  return CKL_OK;
+}
+
+// ------------------------------------------------------------------ timing
+enum Kind { T_LOGITS = 0, T_ROWS, T_DH, T_DHRED, T_DW, T_OTHER, T_KINDS };
+struct TimingState {
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  std::vector<std::pair<int, int>> recs;  // (kind, pool index)
+};
+TimingState g_tm;
+
+struct Timed {
+  int idx = -1;
+  hipStream_t s;
+  Timed(int kind, hipStream_t st) : s(st) {
+    if (!g_tm.on) return;
+    const int i = (int)g_tm.recs.size();
+    if (i >= (int)g_tm.pool.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) return;
+      g_tm.pool.push_back({a, b});
+    }
+    g_tm.recs.push_back({kind, i});
+    idx = i;
+    (void)hipEventRecord(g_tm.pool[i].first, s);
+  }
+  ~Timed() {
+    if (idx >= 0) (void)hipEventRecord(g_tm.pool[idx].second, s);
+  }
+};
+
+#define CKL_TRY(expr)                     \
+  do {                                    \
+    hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return CKL_EHIP; \
+  } while (0)
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, const float* tlogit,
+                 const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
+                 void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream) {
+  if (!H || !W || !ids || !tlogit || !out_loss || !dH || !dW) return CKL_EINVAL;
+  if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return CKL_EINVAL;
+  if (!aligned(ids, 4) || !aligned(tlogit, 4) || !aligned(out_loss, 4)) return CKL_EINVAL;
+  if (!aligned(row_kl, 4) || !aligned(row_lse, 4)) return CKL_EINVAL;
+  Layout L;
+  int st = plan_impl(N, d, V, K, chunk, 0, &L);
+  if (st != CKL_OK) return st;
+  if ((N + L.C - 1) / L.C > (int64_t)1 << 24) return CKL_EUNSUPPORTED;
+
+  int dev = 0;
+  CKL_TRY(hipGetDevice(&dev));
+  void* ws = nullptr;
+  st = get_workspace(dev, stream, L.total, &ws);
+  if (st != CKL_OK) return st;
+  char* base = (char*)ws;
+  float* Z = (float*)(base + L.z_off);
+  float2* part = (float2*)(base + L.part_off);
+  float* slab = (float*)(base + L.slab_off);
+  float* kl = row_kl ? row_kl : (float*)(base + L.kl_off);
+  float* lse = row_lse ? row_lse : (float*)(base + L.lse_off);
+  void* scal = base + L.scal_off;
+  const size_t esz = dt == DT_BF16 ? 2 : 4;
+  const int64_t ldg = dt == DT_BF16 ? 2 * L.ldz : L.ldz;
+
+  {
+    Timed t(T_OTHER, stream);
+    CKL_TRY(launch_mask_count(mask, N, scal, stream));
+  }
+  for (int64_t r0 = 0; r0 < N; r0 += L.C) {
+    const int64_t rows = (N - r0) < L.C ? (N - r0) : L.C;
+    const void* Hc = (const char*)H + (size_t)r0 * d * esz;
+    {
+      Timed t(T_LOGITS, stream);
+      CKL_TRY(launch_logits(dt, W, Hc, V, d, rows, Z, L.ldz, part, L.n_slices, stream));
+    }
+    {
+      RowArgs a{};
+      a.Z = Z;
+      a.ldz = L.ldz;
+      a.part = part;
+      a.n_slices = L.n_slices;
+      a.ids = ids + r0 * K;
+      a.tlogit = tlogit + r0 * K;
+      a.mask = mask ? mask + r0 : nullptr;
+      a.scal = scal;
+      a.V = V;
+      a.K = (int)K;
+      a.rows = rows;
+      a.kl_out = kl + r0;
+      a.lse_out = lse + r0;
+      Timed t(T_ROWS, stream);
+      CKL_TRY(launch_rows(dt, a, stream));
+    }
+    int splits = dh_splits(rows, d, V);
+    const int64_t cap = (int64_t)L.splits * L.C / rows;  // slab capacity in splits of this chunk
+    if (splits > cap) splits = (int)cap;
+    {
+      Timed t(T_DH, stream);
+      CKL_TRY(launch_dh(dt, Z, ldg, W, V, d, rows, slab, splits, stream));
+    }
+    {
+      Timed t(T_DHRED, stream);
+      CKL_TRY(launch_dh_reduce(dt, slab, splits, rows, d, (char*)dH + (size_t)r0 * d * esz, stream));
+    }
+    {
+      Timed t(T_DW, stream);
+      CKL_TRY(launch_dw(dt, Z, ldg, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, stream));
+    }
+  }
+  {
+    Timed t(T_OTHER, stream);
+    CKL_TRY(launch_finalize(kl, N, scal, out_loss, stream));
+  }
+  return CKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ckl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+                const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
+                void* dH, float* dW, hipStream_t stream) {
+  try {
+    return fwd_bwd_impl(DT_BF16, H, W, topk_idx, topk_logit, mask, N, d, V, K, chunk, out_loss, dH, dW, nullptr,
+                        nullptr, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_fwd_bwd_f32(const float* H, const float* W, const int32_t* topk_idx, const float* topk_logit,
+                    const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                    float* out_loss, float* dH, float* dW, hipStream_t stream) {
+  try {
+    return fwd_bwd_impl(DT_F32, H, W, topk_idx, topk_logit, mask, N, d, V, K, chunk, out_loss, dH, dW, nullptr,
+                        nullptr, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+                   const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
+                   void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream) {
+  if (dtype != CKL_DTYPE_BF16 && dtype != CKL_DTYPE_F32) return CKL_EINVAL;
+  try {
+    return fwd_bwd_impl(dtype == CKL_DTYPE_BF16 ? DT_BF16 : DT_F32, H, W, topk_idx, topk_logit, mask, N, d, V, K,
+                        chunk, out_loss, dH, dW, row_kl, row_lse, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
+             int64_t* chunk_out, uint64_t* workspace_bytes_out) {
+  if (dtype != CKL_DTYPE_BF16 && dtype != CKL_DTYPE_F32) return CKL_EINVAL;
+  try {
+    Layout L;
+    const int st = plan_impl(N, d, V, K, chunk, budget_bytes, &L);
+    if (st != CKL_OK) return st;
+    if (chunk_out) *chunk_out = L.C;
+    if (workspace_bytes_out) *workspace_bytes_out = L.total;
+    return CKL_OK;
+  } catch (...) {
+    return CKL_EINVAL;
+  }
+}
+
+void ckl_release_workspace(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr) {
+      int cur = 0;
+      (void)hipGetDevice(&cur);
+      (void)hipSetDevice(kv.first.dev);
+      (void)hipDeviceSynchronize();
+      (void)hipFree(kv.second.ptr);
+      (void)hipSetDevice(cur);
+    }
+  }
+  g_ws.clear();
+}
+
+uint64_t ckl_workspace_bytes_held(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  uint64_t t = 0;
+  for (auto& kv : g_ws) t += kv.second.bytes;
+  return t;
+}
+
+const char* ckl_strerror(int status) {
+  switch (status) {
+    case CKL_OK: return "ok";
+    case CKL_EINVAL: return "invalid argument";
+    case CKL_ENOMEM: return "device workspace allocation failed";
+    case CKL_EBUDGET: return "no chunk size fits the workspace budget";
+    case CKL_EHIP: return "HIP runtime error";
+    case CKL_EUNSUPPORTED: return "unsupported shape";
+    default: return "unknown status";
+  }
+}
+
+int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, const uint8_t* mask, int64_t R,
+                   int64_t V, int64_t K, float scale, int g_bf16, float* zg_out, int32_t* scatter_ids_out,
+                   void* G_out, float* kl_out, float* lse_out, hipStream_t stream) {
+  try {
+    if (!Z || !idx || !tlogit || !zg_out || !scatter_ids_out || !G_out || !kl_out || !lse_out) return CKL_EINVAL;
+    if (R <= 0 || V <= 0 || K <= 0 || K > V) return CKL_EINVAL;
+    if (K > kMaxK) return CKL_EUNSUPPORTED;
+    if (R > (int64_t)1 << 20 || V > (int64_t)1 << 30) return CKL_EUNSUPPORTED;
+    const int64_t ldz = roundup(V, 64);
+    const int n_slices = (int)((V + 127) / 128);
+    const uint64_t zb = align256((uint64_t)R * ldz * 4), pb = align256((uint64_t)R * n_slices * 8);
+    int dev = 0;
+    CKL_TRY(hipGetDevice(&dev));
+    void* ws = nullptr;
+    int st = get_workspace(dev, stream, zb + pb, &ws);
+    if (st != CKL_OK) return st;
+    float* Zw = (float*)ws;
+    float2* part = (float2*)((char*)ws + zb);
+    CKL_TRY(hipMemcpy2DAsync(Zw, ldz * 4, Z, V * 4, V * 4, R, hipMemcpyDeviceToDevice, stream));
+    CKL_TRY(launch_partials_from_z(Zw, ldz, R, V, part, n_slices, stream));
+    RowArgs a{};
+    a.Z = Zw;
+    a.ldz = ldz;
+    a.part = part;
+    a.n_slices = n_slices;
+    a.ids = idx;
+    a.tlogit = tlogit;
+    a.mask = mask;
+    a.scal = nullptr;
+    a.scale_value = scale;
+    a.V = V;
+    a.K = (int)K;
+    a.rows = R;
+    a.kl_out = kl_out;
+    a.lse_out = lse_out;
+    a.zg_dbg = zg_out;
+    a.sid_dbg = scatter_ids_out;
+    CKL_TRY(launch_rows(g_bf16 ? DT_BF16 : DT_F32, a, stream));
+    const size_t esz = g_bf16 ? 2 : 4;
+    CKL_TRY(hipMemcpy2DAsync(G_out, V * esz, Zw, ldz * 4, V * esz, R, hipMemcpyDeviceToDevice, stream));
+    CKL_TRY(hipStreamSynchronize(stream));
+    return CKL_OK;
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_timing_enable(int on) {
+  g_tm.on = on != 0;
+  g_tm.recs.clear();
+  return CKL_OK;
+}
+
+int ckl_timing_query(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= T_KINDS || !total_ms || !launches) return CKL_EINVAL;
+  double t = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_tm.recs) {
+    if (r.first != kind) continue;
+    auto& ev = g_tm.pool[r.second];
+    if (hipEventSynchronize(ev.second) != hipSuccess) return CKL_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess) return CKL_EHIP;
+    t += ms;
+    ++n;
+  }
+  *total_ms = t;
+  *launches = n;
+  return CKL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// Instantiations and launchers of the three contractions of the loss.
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace ckl {
+
+namespace {
+
+constexpr int kGroupM = 4;
+
+inline int cdiv64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI>
+hipError_t run(GemmParams& p, hipStream_t s) {
+  const int total = p.tiles_m * p.tiles_n * p.splits;
+  const int grid = ((total + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI>), dim3(grid), dim3(WM * WN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int d_tile(int64_t d) { return (d % 192 == 0 && d % 256 != 0) ? 192 : 256; }
+
+int dh_splits(int64_t rows, int64_t d, int64_t V) {
+  // Pick the k-split count (1..8) that best fills whole waves of 256
+  // workgroups; each split keeps at least 16 k-steps.
+  const int tiles = cdiv64(rows, 256) * cdiv64(d, d_tile(d));
+  const int ksteps = cdiv64(V, 64);
+  int best = 1;
+  double best_eff = -1.0;
+  for (int s = 1; s <= 8; ++s) {
+    if (s > 1 && ksteps / s < 16) break;
+    const double waves = (double)tiles * s / 256.0;
+    const double eff = waves / (double)((int64_t)(waves + 0.999999));
+    if (eff > best_eff + 0.02) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int64_t d, int64_t rows,
+                         float* Z, int64_t ldz, float2* part, int n_slices, hipStream_t s) {
+  GemmParams p{};
+  p.a = Operand{W, d, V, d};
+  p.b = Operand{Hc, d, rows, d};
+  p.tiles_m = cdiv64(V, 256);
+  p.tiles_n = cdiv64(rows, 256);
+  const int bk = dt == DT_BF16 ? 64 : 32;
+  p.k_tiles = cdiv64(d, bk);
+  p.splits = 1;
+  p.k_tiles_per_split = p.k_tiles;
+  p.group_m = kGroupM;
+  p.out = Z;
+  p.ldo = ldz;
+  p.valid_m = V;
+  p.valid_n = rows;
+  p.part = part;
+  p.n_slices = n_slices;
+  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, true, true, EPI_LOGITS>(p, s);
+  return run<float, 256, 256, 2, 4, true, true, EPI_LOGITS>(p, s);
+}
+
+hipError_t launch_dh(Dtype dt, const void* G, int64_t ldg, const void* W, int64_t V, int64_t d, int64_t rows,
+                     float* slab, int splits, hipStream_t s) {
+  const int64_t vpad = (V + 7) / 8 * 8;
+  const int bn = d_tile(d);
+  const int bk = dt == DT_BF16 ? 64 : 32;
+  GemmParams p{};
+  p.a = Operand{G, ldg, rows, vpad};
+  p.b = Operand{W, d, d, V};
+  p.tiles_m = cdiv64(rows, 256);
+  p.tiles_n = cdiv64(d, bn);
+  p.k_tiles = cdiv64(V, bk);
+  p.k_tiles_per_split = cdiv64(p.k_tiles, splits);
+  p.splits = cdiv64(p.k_tiles, p.k_tiles_per_split);
+  p.group_m = kGroupM;
+  p.out = slab;
+  p.ldo = d;
+  p.split_stride = rows * d;
+  p.valid_m = rows;
+  p.valid_n = d;
+  if (p.splits != splits) return hipErrorInvalidValue;
+  if (dt == DT_BF16) {
+    if (bn == 192) return run<__bf16, 256, 192, 4, 2, true, false, EPI_SLAB>(p, s);
+    return run<__bf16, 256, 256, 4, 2, true, false, EPI_SLAB>(p, s);
+  }
+  if (bn == 192) return run<float, 256, 192, 4, 2, true, false, EPI_SLAB>(p, s);
+  return run<float, 256, 256, 4, 2, true, false, EPI_SLAB>(p, s);
+}
+
+hipError_t launch_dw(Dtype dt, const void* G, int64_t ldg, const void* Hc, int64_t V, int64_t d, int64_t rows,
+                     float* dW, int beta, hipStream_t s) {
+  const int64_t vpad = (V + 7) / 8 * 8;
+  const int bn = d_tile(d);
+  const int bk = dt == DT_BF16 ? 64 : 32;
+  GemmParams p{};
+  p.a = Operand{G, ldg, vpad, rows};
+  p.b = Operand{Hc, d, d, rows};
+  p.tiles_m = cdiv64(V, 256);
+  p.tiles_n = cdiv64(d, bn);
+  p.k_tiles = cdiv64(rows, bk);
+  p.splits = 1;
+  p.k_tiles_per_split = p.k_tiles;
+  p.group_m = kGroupM;
+  p.out = dW;
+  p.ldo = d;
+  p.valid_m = V;
+  p.valid_n = d;
+  p.beta = beta;
+  if (dt == DT_BF16) {
+    if (bn == 192) return run<__bf16, 256, 192, 4, 2, false, false, EPI_ACCUM>(p, s);
+    return run<__bf16, 256, 256, 4, 2, false, false, EPI_ACCUM>(p, s);
+  }
+  if (bn == 192) return run<float, 256, 192, 4, 2, false, false, EPI_ACCUM>(p, s);
+  return run<float, 256, 256, 4, 2, false, false, EPI_ACCUM>(p, s);
+}
+
+// ---------------------------------------------------------------- split-K reduce
+template <typename TO>
+__global__ void __launch_bounds__(256) dh_reduce_kernel(const float* __restrict__ slab, int splits, int64_t count,
+                                                       TO* __restrict__ out) {
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= count) return;
+  f32x4 acc = *(const f32x4*)(slab + i4);
+  for (int s = 1; s < splits; ++s) acc += *(const f32x4*)(slab + (int64_t)s * count + i4);
+  if constexpr (sizeof(TO) == 4) {
+    *(f32x4*)((float*)out + i4) = acc;
+  } else {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+    bf16x4 v = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
+    *(bf16x4*)((__bf16*)out + i4) = v;
+  }
+}
+
+hipError_t launch_dh_reduce(Dtype dt, const float* slab, int splits, int64_t rows, int64_t d, void* dH,
+                            hipStream_t s) {
+  const int64_t count = rows * d;  // d % 8 == 0, so count % 4 == 0
+  const int64_t blocks = (count / 4 + 255) / 256;
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(dh_reduce_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, slab, splits, count,
+                       (__bf16*)dH);
+  else
+    hipLaunchKernelGGL(dh_reduce_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, slab, splits, count,
+                       (float*)dH);
+  return hipGetLastError();
+}
+
+}  // namespace ckl

@@ -188,7 +188,7 @@ def _ids(ss, wl, N, H, W):
         cdf = _zipf_cdf(V, 1.1)
         return _distinct_rows(ss, N, K, V,
                               lambda u: np.minimum(np.searchsorted(cdf, u, side="right"), V - 1),
-                              batch=2048)
+                              batch=256)
     if wl.ids == "overlap50":
         half = K // 2
         s_pick, s_rest, s_perm = ss.spawn(3)

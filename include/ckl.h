@@ -1,0 +1,144 @@
+/*
+ * ckl.h -- C ABI of the fused chunked KL distillation loss for MI355X (gfx950).
+ *
+ * The loss compares a student's full-vocabulary distribution with an offline
+ * cache of the teacher's top-K logits per position and returns the loss with
+ * its gradients, without ever holding the student's vocabulary x sequence
+ * logit grid: the sequence is processed in row chunks and each chunk's logits
+ * are computed, turned into gradient and discarded before the next chunk
+ * ("A New Trick Slashes the Cost of Shrinking Giant AI Models", sections
+ * "What did the researchers change?" and "Does this matter for longer
+ * documents?"; "Making Knowledge Distillation Cheap Enough to Run at Scale"
+ * (aiphreaks.com), bullet "Fused Chunked KL Loss").
+ *
+ * Definition (the readings where the pages are silent are stated here):
+ *   z_r      = H_r . W^T                        student logits of position r, length V
+ *   log p_S  = z_r - logsumexp(z_r)             full-vocabulary log-softmax
+ *   p_T      = softmax(T_r)                     over the K cached teacher logits only;
+ *                                               the other V - K tokens get no mass
+ *                                               (elseif.net page, limitations paragraph)
+ *   KL_r     = sum_k p_T,k (log p_T,k - log p_S,id_k)
+ *   loss     = (1 / n) sum_r mask_r KL_r,       n = number of valid positions
+ *                                               (loss = 0 and all gradients 0 if n = 0)
+ *   dL/dz_r  = (mask_r / n) (softmax(z_r) - scatter(p_T,r))
+ *   dH       = G W,   dW = G^T H                with G the stacked dL/dz_r
+ * Temperature 1.  Teacher ids within a row must be distinct and in [0, V).
+ *
+ * Layout and ownership (every call):
+ *   - all arrays are row-major and contiguous, in device memory of the device
+ *     that is current on the calling thread, and `stream` belongs to it;
+ *   - H, W, dH, dW must be 16-byte aligned; ids, logits, out_loss 4-byte;
+ *   - the caller owns every buffer; the library keeps no pointer after the
+ *     call returns.  Work is enqueued on `stream` with no host synchronisation,
+ *     so inputs and outputs must stay alive until the stream has finished;
+ *   - d must be a multiple of 8; 1 <= K <= min(V, 2048);
+ *   - the library holds one grow-only device workspace per (device, stream),
+ *     sized by ckl_plan; ckl_release_workspace frees them all.
+ *
+ * Errors: arguments that are invalid or not supported are reported before
+ * anything is enqueued, and the outputs are untouched.  A HIP failure returns
+ * CKL_EHIP or CKL_ENOMEM and leaves the outputs undefined; since every call
+ * overwrites dW (it does not accumulate into it), the call can be repeated.
+ * No C++ exception crosses this interface.
+ */
+#ifndef CKL_H_
+#define CKL_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CKL_OK = 0,
+  CKL_EINVAL = -1,       /* null or misaligned pointer, non-positive size, K > V, chunk < 0 */
+  CKL_ENOMEM = -2,       /* device workspace allocation failed */
+  CKL_EBUDGET = -3,      /* no chunk size fits the workspace budget (or the given chunk does not) */
+  CKL_EHIP = -4,         /* a HIP runtime call failed */
+  CKL_EUNSUPPORTED = -5  /* d % 8 != 0, K > 2048, or a size beyond 32-bit grid limits */
+} ckl_status;
+
+typedef enum { CKL_DTYPE_BF16 = 0, CKL_DTYPE_F32 = 1 } ckl_dtype;
+
+/* Fused forward + backward of the loss above (bf16 hidden states and weight).
+ *   H          bf16 [N, d]   student final hidden states
+ *   W          bf16 [V, d]   LM-head weight
+ *   topk_idx   int32 [N, K]  cached teacher ids, distinct per row, in [0, V)
+ *   topk_logit fp32 [N, K]   cached teacher logits
+ *   mask       uint8 [N]     1 = position counts, 0 = ignored; NULL = all count
+ *   chunk      rows per chunk; 0 lets ckl_plan choose under the workspace budget
+ *              (environment CKL_WORKSPACE_BYTES, default 6 GiB)
+ *   out_loss   fp32 device scalar
+ *   dH         bf16 [N, d]   gradient of the loss with respect to H (overwritten)
+ *   dW         fp32 [V, d]   gradient with respect to W (overwritten)
+ * The pages' interface statement is that a training code only swaps in this
+ * loss, fed by the precomputed top-K cache (elseif.net page, adoption paragraph). */
+int ckl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+                const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                float* out_loss, void* dH, float* dW, hipStream_t stream);
+
+/* Same as ckl_fwd_bwd with H, W and dH in fp32 (fp32 matrix cores). */
+int ckl_fwd_bwd_f32(const float* H, const float* W, const int32_t* topk_idx, const float* topk_logit,
+                    const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                    float* out_loss, float* dH, float* dW, hipStream_t stream);
+
+/* ckl_fwd_bwd / ckl_fwd_bwd_f32 selected by `dtype` (ckl_dtype), with two
+ * optional per-position outputs (device, caller-owned, may be NULL):
+ *   row_kl   fp32 [N]  KL_r of each position (0 for masked positions)
+ *   row_lse  fp32 [N]  logsumexp of the student logits of each position
+ * The loss is the sum of row_kl divided by the valid count. */
+int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+                   const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
+                   float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream);
+
+/* Chunk planner (pure host computation, needs no GPU).  The sequence is cut
+ * into chunks of C rows so that the loss's own device memory stays bounded
+ * independently of N ("A New Trick...", section "Does this matter for longer
+ * documents?": peak memory stays almost flat as inputs grow).
+ *   chunk         > 0: use min(chunk, N) rows, CKL_EBUDGET if it does not fit;
+ *                 0: the largest multiple of 256 rows that fits (or N if
+ *                 N < 256), then evened out over the resulting chunk count
+ *   budget_bytes  0 = CKL_WORKSPACE_BYTES or 6 GiB
+ *   chunk_out, workspace_bytes_out  (may be NULL) chosen rows, exact bytes the
+ *                 call will allocate for its workspace */
+int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
+             int64_t* chunk_out, uint64_t* workspace_bytes_out);
+
+/* Frees every cached workspace (after synchronising the device). */
+void ckl_release_workspace(void);
+
+/* Bytes currently held in cached workspaces (all devices and streams). */
+uint64_t ckl_workspace_bytes_held(void);
+
+/* Human-readable name of a status code. */
+const char* ckl_strerror(int status);
+
+/* Test entry: the row pass alone on caller-given fp32 logits Z [R, V]
+ * (row stride V): log-normaliser, teacher softmax, gather, KL and the logit
+ * gradient with weight `scale` for rows whose mask is 1 (or all rows if mask
+ * is NULL).  Outputs (device, caller-owned):
+ *   zg_out          fp32 [R, K]  the logits gathered at the teacher ids
+ *   scatter_ids_out int32 [R, K] the ids the top-K values were scattered to
+ *   G_out           [R, V]       gradient, bf16 if g_bf16 else fp32
+ *   kl_out, lse_out fp32 [R]     per-row KL (0 for masked rows) and logsumexp
+ * Synchronises `stream` before returning. */
+int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, const uint8_t* mask, int64_t R,
+                   int64_t V, int64_t K, float scale, int g_bf16, float* zg_out, int32_t* scatter_ids_out,
+                   void* G_out, float* kl_out, float* lse_out, hipStream_t stream);
+
+/* Measurement support.  While enabled, every kernel launch of a fwd_bwd call
+ * is bracketed by HIP events on the call's stream.  ckl_timing_query waits for
+ * the recorded events and returns the summed milliseconds and launch count of
+ * one kernel kind: 0 logits GEMM, 1 row pass, 2 dH GEMM, 3 dH split reduce,
+ * 4 dW GEMM, 5 other.  Not for concurrent use from several threads. */
+int ckl_timing_enable(int on);
+int ckl_timing_query(int kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKL_H_ */

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI: symbols, planner arithmetic and argument errors (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_kl_loss_seq_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libckl.so not built")
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "ckl.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckl_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = B.lib()
+    names = declared_functions()
+    assert "ckl_fwd_bwd" in names and "ckl_plan" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror():
+    assert B.strerror(0) == "ok"
+    assert "budget" in B.strerror(-3)
+    assert B.strerror(12345) == "unknown status"
+
+
+GiB = 1 << 30
+
+
+def ws_formula(N, d, V, C, splits):
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    ldz = (V + 63) // 64 * 64
+    nsl = (V + 127) // 128
+    return a(C * ldz * 4) + a(C * nsl * 8) + a(splits * C * d * 4) + 2 * a(N * 4) + 256
+
+
+def test_plan_explicit_chunk_matches_formula():
+    for (N, d, V, K, C) in [(256, 256, 4096, 16, 64), (4096, 2048, 32000, 100, 1024), (600, 200, 1003, 37, 256)]:
+        c, ws = B.plan(N, d, V, K, chunk=C)
+        assert c == min(C, N)
+        # the dH split count is 1..8; the bytes must match the formula for one of them
+        assert any(ws == ws_formula(N, d, V, c, s) for s in range(1, 9)), (N, d, V, ws)
+
+
+def test_plan_gpt_oss_head_fits_six_gib():
+    c, ws = B.plan(32768, 2880, 201088, 100)
+    assert ws <= 6 * GiB
+    assert c % 256 == 0 and c > 0
+    # a chunk one 256-row step larger would not fit, or the chunks were evened out
+    nch = -(-32768 // c)
+    assert nch * c >= 32768 and (nch - 1) * c < 32768
+    # the long batch gets the same chunk: the workspace does not grow with N
+    c5, ws5 = B.plan(131072, 2880, 201088, 100)
+    assert ws5 <= 6 * GiB
+    assert abs(ws5 - ws) < 4 * 131072 * 2 + 1 << 20 or c5 != c
+
+
+def test_plan_workspace_bounded_in_sequence_length():
+    # peak workspace stays under the budget at any N; the chunk count grows instead
+    prev_chunks = 0
+    for N in (16384, 32768, 65536, 131072, 262144):
+        c, ws = B.plan(N, 2880, 201088, 100)
+        assert ws <= 6 * GiB
+        n_chunks = -(-N // c)
+        assert n_chunks >= prev_chunks
+        prev_chunks = n_chunks
+    assert prev_chunks >= 262144 // 8192
+
+
+def test_plan_budget_errors():
+    with pytest.raises(B.CklError) as e:
+        B.plan(32768, 2880, 201088, 100, budget_bytes=100 << 20)
+    assert e.value.status == -3
+    with pytest.raises(B.CklError) as e:
+        B.plan(32768, 2880, 201088, 100, chunk=16384)  # 16384 x 201088 x 4 B > 6 GiB
+    assert e.value.status == -3
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 8, 10, 1), -1), ((4, 0, 10, 1), -1), ((4, 8, 0, 1), -1), ((4, 8, 10, 0), -1),
+    ((4, 8, 10, 11), -1), ((4, 12, 10, 2), -5), ((4, 8, 5000, 3000), -5),
+])
+def test_plan_argument_errors(args, status):
+    with pytest.raises(B.CklError) as e:
+        B.plan(*args)
+    assert e.value.status == status
+
+
+def test_plan_negative_chunk():
+    with pytest.raises(B.CklError) as e:
+        B.plan(4, 8, 10, 2, chunk=-1)
+    assert e.value.status == -1
+
+
+def test_fwd_bwd_rejects_bad_pointers_before_any_gpu_call():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = vp(1 << 20)
+    # null H
+    st = L.ckl_fwd_bwd(vp(0), good, good, good, vp(0), 4, 8, 10, 2, 0, good, good, good, vp(0))
+    assert st == -1
+    # misaligned W
+    st = L.ckl_fwd_bwd(good, vp((1 << 20) + 2), good, good, vp(0), 4, 8, 10, 2, 0, good, good, good, vp(0))
+    assert st == -1
+    # K > V
+    st = L.ckl_fwd_bwd(good, good, good, good, vp(0), 4, 8, 10, 11, 0, good, good, good, vp(0))
+    assert st == -1
+    # d not a multiple of 8
+    st = L.ckl_fwd_bwd_f32(good, good, good, good, vp(0), 4, 12, 10, 2, 0, good, good, good, vp(0))
+    assert st == -5
+    # unknown dtype
+    st = L.ckl_fwd_bwd_ex(7, good, good, good, good, vp(0), 4, 8, 10, 2, 0, good, good, good, vp(0), vp(0), vp(0))
+    assert st == -1
+
+
+def test_timing_query_argument_check():
+    L = B.lib()
+    t = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    assert L.ckl_timing_query(99, ctypes.byref(t), ctypes.byref(n)) == -1
+    assert B.timing_enable(False) is None
