@@ -4,15 +4,18 @@
 //   dH        dH_c     = G . W       (G contiguous along V, W contiguous along d)
 //   dW        dW      += G^T . H_c   (both operands contiguous along the token axis)
 //
-// One workgroup computes a BM x BN tile of D = A . B with WM x WN waves.  Each
-// k-step stages a BK-deep slab of A and B through LDS (double buffered):
-//   * an operand contiguous along k ("k-major") is kept as [row][128 bytes]
+// One workgroup computes a BM x BN tile of D = A . B with WM x WN waves.  The
+// reduction runs over k-slabs of BK = KB / sizeof(T) elements, copied global ->
+// LDS by buffer_load ... lds into a ring of NS stages, so NS - 1 slabs are in
+// flight while one is consumed:
+//   * an operand contiguous along k ("k-major") is kept as [row][KB bytes]
 //     with a 16-byte-chunk XOR swizzle and read as one ds_read_b128 per MFMA
 //     fragment;
 //   * an operand contiguous along m or n ("mn-major") is kept as it lies in
-//     memory, [k][row] with a 32-byte row pad, and read with ds_read_tr16_b64,
-//     which hands each lane four k-consecutive 16-bit values of one column
-//     (two reads per bf16 fragment).  fp32 mn-major operands use ds_read_b32.
+//     memory, [k][row], with a 64-byte-block XOR swizzle, and read with
+//     ds_read_tr16_b64, which hands each lane four k-consecutive 16-bit values
+//     of one column (two reads per bf16 fragment).  fp32 mn-major operands use
+//     ds_read_b32.
 // bf16 operands use v_mfma_f32_32x32x16_bf16; fp32 operands use
 // v_mfma_f32_32x32x2_f32 over the same LDS layout: a fragment holds the
 // 8 k-values k0 + 8h .. k0 + 8h + 7 of lane half h in both cases, and the
@@ -70,75 +73,128 @@ struct GemmParams {
   int beta;              // EPI_ACCUM
 };
 
-template <typename T>
-struct ElemTraits;
-template <>
-struct ElemTraits<__bf16> {
-  static constexpr int kBK = 64;  // k elements per 128-byte row
-};
-template <>
-struct ElemTraits<float> {
-  static constexpr int kBK = 32;
-};
-
 // ---------------------------------------------------------------- LDS layouts
-template <typename T, int R, bool KMAJ>
-struct TileLayout;
-
-// k-major: [R rows][128 bytes], chunk c of row r stored at chunk c ^ (r & 7).
-template <typename T, int R>
-struct TileLayout<T, R, true> {
-  static constexpr int kBytes = R * 128;
-  __device__ static inline int off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// One wave instruction of buffer_load ... lds moves 1 KiB, lane l's 16 bytes
+// landing at byte 16 l of that KiB, so the LDS layouts are fixed by which
+// global chunk each lane fetches.  The swizzles keep the fragment reads free of
+// bank conflicts on gfx950's 64-bank (256 bytes per clock) LDS, which serves a
+// ds_read_b128 16 lanes at a time and a ds_read_b64 32 lanes at a time.
+//
+// k-major slab: [R rows][KB bytes]; the 16-byte chunk c of row r sits at
+// chunk c ^ ((r / (256 / KB)) % (KB / 16)): the 16 rows one fragment read
+// serves together fall on 16 distinct 16-byte bank groups.
+template <int R, int KB>
+struct KTile {
+  static constexpr int kCPR = KB / 16;          // chunks per row
+  static constexpr int kRowsPerBankRow = 256 / KB;
+  static constexpr int kBytes = R * KB;
+  __device__ static inline int off(int row, int chunk) {
+    return row * KB + ((chunk ^ ((row / kRowsPerBankRow) % kCPR)) << 4);
+  }
 };
 
-// mn-major: [BK k-rows][R * sizeof(T) + 32 bytes].  The 32-byte pad puts the
-// four k-rows one ds_read_tr16_b64 group touches in distinct bank quarters.
-template <typename T, int R>
-struct TileLayout<T, R, false> {
-  static constexpr int kPitch = R * (int)sizeof(T) + 32;
-  static constexpr int kBytes = ElemTraits<T>::kBK * kPitch;
-  __device__ static inline int off(int krow, int chunk) { return krow * kPitch + chunk * 16; }
+// mn-major slab: [BK k-rows][R * sizeof(T) bytes]; the 64-byte block j of
+// k-row k sits at block j ^ swz(k).  A ds_read_tr16_b64 serves 32 lanes that
+// read the same 64-byte block of 4 consecutive k-rows; swz puts those four
+// blocks in the four distinct 64-byte bank quarters.
+template <typename T, int R, int BK>
+struct MNTile {
+  static constexpr int kRowBytes = R * (int)sizeof(T);
+  static constexpr int kBytes = BK * kRowBytes;
+  static constexpr int kStep = (kRowBytes / 64) % 4;  // bank quarter advance per k-row
+  static_assert(kRowBytes % 256 == 0 || kRowBytes % 256 == 128, "unsupported mn-major tile width");
+  __device__ static inline int swz(int k) { return kStep == 0 ? (k & 3) : ((k >> 1) & 1); }
+  // byte address of logical byte lb (= column * sizeof(T)) of k-row k
+  __device__ static inline int off(int k, int lb) { return k * kRowBytes + ((((lb >> 6) ^ swz(k)) << 6) | (lb & 63)); }
 };
 
-// ---------------------------------------------------------------- global -> registers
-// Each thread carries NCH 16-byte chunks of the tile in flight.
-template <typename T, int R, int NT, bool KMAJ>
-struct TileLoader {
-  static constexpr int kEPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
-  static constexpr int kChunks = R * 8;                      // 128 bytes of k per row, or BK rows of R
-  static constexpr int kNCH = kChunks / NT;
-  static_assert(kChunks % NT == 0, "tile chunks must divide evenly over the workgroup");
-  static constexpr int kCPR = KMAJ ? 8 : R * (int)sizeof(T) / 16;  // chunks per stored row
+// ---------------------------------------------------------------- global -> LDS
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at their "no wait" maxima).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-  __device__ static inline void load(u32x4 (&r)[kNCH], const Operand& o, int64_t mn0, int64_t k0, int tid) {
-    const T* base = (const T*)o.ptr;
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past the range: the load returns zeros
+
+// The base is wave-uniform; readfirstlane makes that explicit so the
+// resource lives in SGPRs (otherwise every load gets a waterfall loop).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7FFFFFF0, 0x00020000);
+}
+
+// Per-lane state to copy one operand's k-slabs of a tile into LDS.  Lane
+// offsets are relative to the slab origin and do not change along k; rows
+// past mn_ext are folded in as out-of-range offsets, k past k_ext is checked
+// on the last slabs only.  The slab's 1 KiB blocks are dealt to the waves in
+// turn; when they do not divide evenly, a wave short of a block issues an
+// out-of-range load into a spare 1 KiB of LDS instead, so that every wave has
+// the same number of loads in flight per slab.
+template <typename T, int R, int NW, bool KMAJ, int KB>
+struct SlabDMA {
+  static constexpr int kEPC = 16 / (int)sizeof(T);
+  static constexpr int kBK = KB / (int)sizeof(T);
+  static constexpr int kBytes = KMAJ ? KTile<R, KB>::kBytes : MNTile<T, R, kBK>::kBytes;
+  static constexpr int kBlocks = kBytes / 1024;
+  static constexpr int kNI = (kBlocks + NW - 1) / NW;  // load instructions per wave per slab (at most)
+  static constexpr bool kEven = kBlocks % NW == 0;
+  static_assert(kBytes % 1024 == 0, "slab must be whole KiB blocks");
+
+  uint32_t voff[kNI];
+  uint8_t kd[kNI];  // k offset of this lane's chunk within the slab
+
+  __device__ static inline bool has(int wave, int i) { return kEven || i * NW + wave < kBlocks; }
+  static constexpr int kSpare = kEven ? 0 : 1024;  // LDS bytes for the padding loads
+
+  __device__ inline void init(const Operand& o, int64_t mn0, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < kNCH; ++i) {
-      const int idx = tid + i * NT;
-      const int srow = idx / kCPR, c = idx % kCPR;
-      int64_t mn, k;
+    for (int i = 0; i < kNI; ++i) {
+      const int b = i * NW + wave;
+      int row_mn, kdel;
       if (KMAJ) {
-        mn = mn0 + srow;
-        k = k0 + (int64_t)c * kEPC;
+        typedef KTile<R, KB> L;
+        const int q = b * 1024 + lane * 16;
+        const int row = q / KB;
+        const int pc = (q % KB) >> 4;
+        const int c = pc ^ ((row / L::kRowsPerBankRow) % L::kCPR);
+        row_mn = row;
+        kdel = c * kEPC;
+        voff[i] = (uint32_t)((int64_t)row * o.ld * (int64_t)sizeof(T) + c * 16);
       } else {
-        k = k0 + srow;
-        mn = mn0 + (int64_t)c * kEPC;
+        typedef MNTile<T, R, kBK> L;
+        const int q = b * 1024 + lane * 16;
+        const int krow = q / L::kRowBytes;
+        const int pb = q % L::kRowBytes;
+        const int lb = (((pb >> 6) ^ L::swz(krow)) << 6) | (pb & 63);
+        row_mn = lb / (int)sizeof(T);
+        kdel = krow;
+        voff[i] = (uint32_t)((int64_t)krow * o.ld * (int64_t)sizeof(T) + lb);
       }
-      const bool ok = (mn < o.mn_ext) && (k < o.k_ext);
-      const int64_t e = KMAJ ? (mn * o.ld + k) : (k * o.ld + mn);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const u32x4*)(base + e);
-      r[i] = v;
+      kd[i] = (uint8_t)kdel;
+      if (mn0 + row_mn >= o.mn_ext) voff[i] = kOOB;
     }
   }
 
-  __device__ static inline void store(char* lds, const u32x4 (&r)[kNCH], int tid) {
+  // Issue the copy of slab origin k0 into `lds` (a wave-uniform LDS address);
+  // `spare` is 1 KiB of LDS that padding loads may overwrite.
+  __device__ inline void issue(const Operand& o, int64_t mn0, int64_t k0, char* lds, int wave, char* spare) const {
+    const T* base = (const T*)o.ptr + (KMAJ ? (mn0 * o.ld + k0) : (k0 * o.ld + mn0));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const bool tail = k0 + kBK > o.k_ext;
+    const int kleft = tail ? (int)(o.k_ext - k0) : kBK;  // <= 0 when the slab is past the end
 #pragma unroll
-    for (int i = 0; i < kNCH; ++i) {
-      const int idx = tid + i * NT;
-      const int srow = idx / kCPR, c = idx % kCPR;
-      *(u32x4*)(lds + TileLayout<T, R, KMAJ>::off(srow, c)) = r[i];
+    for (int i = 0; i < kNI; ++i) {
+      const bool real = has(wave, i);
+      uint32_t v = voff[i];
+      if (!real || (tail && (int)kd[i] >= kleft)) v = kOOB;
+      char* dst = real ? lds + (i * NW + wave) * 1024 : spare;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, v, 0, 0, 0);
     }
   }
 };
@@ -155,15 +211,13 @@ struct Frag<float> {
   typedef f32x8 type;
 };
 
-// Fragment of 32 rows (rows row0 .. row0+31 of the tile) x 16 k (sub-step kk).
-template <typename T, int R, bool KMAJ>
-__device__ inline typename Frag<T>::type load_frag(const char* lds, int row0, int kk, int lane);
-
-template <typename T, int R, bool KMAJ>
+// Fragment of 32 rows (row0 .. row0+31 of the tile) x 16 k (sub-step kk):
+// lane l gets row row0 + l % 32, k = 16 kk + 8 (l / 32) .. + 7.
+template <typename T, int R, bool KMAJ, int KB>
 __device__ inline typename Frag<T>::type load_frag(const char* lds, int row0, int kk, int lane) {
-  typedef TileLayout<T, R, KMAJ> L;
   const int h = lane >> 5;
   if constexpr (KMAJ) {
+    typedef KTile<R, KB> L;
     const int row = row0 + (lane & 31);
     if constexpr (sizeof(T) == 2) {
       u32x4 v = *(const u32x4*)(lds + L::off(row, 2 * kk + h));
@@ -177,15 +231,16 @@ __device__ inline typename Frag<T>::type load_frag(const char* lds, int row0, in
       return f;
     }
   } else {
+    typedef MNTile<T, R, KB / (int)sizeof(T)> L;
     if constexpr (sizeof(T) == 2) {
-      // 16-lane group g: column block (g & 1) * 16, k block (g >> 1) * 8.
+      // 16-lane group g: columns (g & 1) * 16 .., k block (g >> 1) * 8.
       // Within the group, source lane 4j + p reads k-row j (+4 for the second
       // read) at columns 4p .. 4p+3; the transpose hands lane i column i.
       const int g = lane >> 4, i = lane & 15;
       const int krow = 16 * kk + (g >> 1) * 8 + (i >> 2);
-      const int col = row0 + (g & 1) * 16 + 4 * (i & 3);
-      const char* p0 = lds + krow * L::kPitch + col * 2;
-      const char* p1 = p0 + 4 * L::kPitch;
+      const int lb = (row0 + (g & 1) * 16 + 4 * (i & 3)) * 2;
+      const char* p0 = lds + L::off(krow, lb);
+      const char* p1 = lds + L::off(krow + 4, lb);
       i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
       i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
       u32x4 v;
@@ -196,10 +251,10 @@ __device__ inline typename Frag<T>::type load_frag(const char* lds, int row0, in
       v.w = h2.y;
       return __builtin_bit_cast(bf16x8, v);
     } else {
-      const int col = row0 + (lane & 31);
+      const int lb = (row0 + (lane & 31)) * 4;
       f32x8 f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = *(const float*)(lds + (16 * kk + 8 * h + j) * L::kPitch + col * 4);
+      for (int j = 0; j < 8; ++j) f[j] = *(const float*)(lds + L::off(16 * kk + 8 * h + j, lb));
       return f;
     }
   }
@@ -247,25 +302,30 @@ __device__ inline TileCoord tile_coord(const GemmParams& p) {
 }
 
 // ---------------------------------------------------------------- the kernel
-template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
 __global__ void __launch_bounds__(WM* WN * 64) gemm_kernel(GemmParams p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = ElemTraits<T>::kBK;
+  constexpr int NW = WM * WN;
+  constexpr int BK = KB / (int)sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int SUB = BK / 16;
-  typedef TileLayout<T, BM, AK> LA;
-  typedef TileLayout<T, BN, BKM> LB;
-  typedef TileLoader<T, BM, NT, AK> GA;
-  typedef TileLoader<T, BN, NT, BKM> GB;
+  constexpr int NMF = FM * FN;
+  typedef SlabDMA<T, BM, NW, AK, KB> DA;
+  typedef SlabDMA<T, BN, NW, BKM, KB> DB;
+  constexpr int NIT = DA::kNI + DB::kNI;  // this wave's loads per slab
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(SUB % 2 == 0 && SUB >= 2, "the pipeline assumes an even sub-step count");
+  static_assert(NS >= 2 && (NS - 1) * NIT < 64, "stages in flight must fit the vmcnt counter");
   static_assert(EPI != EPI_LOGITS || WTM == 128, "logit partials are per 128-row slice");
-  constexpr int STAGE = LA::kBytes + LB::kBytes;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int STAGE = DA::kBytes + DB::kBytes;
+  constexpr int SPARE = DA::kSpare > DB::kSpare ? DA::kSpare : DB::kSpare;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + SPARE];
+  char* spare = smem + NS * STAGE;
 
   const TileCoord tc = tile_coord(p);
   if (!tc.valid) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int kt_begin = tc.split * p.k_tiles_per_split;
@@ -279,111 +339,166 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[GA::kNCH], rb[GB::kNCH];
-  GA::load(ra, p.a, m0, (int64_t)kt_begin * BK, tid);
-  GB::load(rb, p.b, n0, (int64_t)kt_begin * BK, tid);
-  GA::store(smem, ra, tid);
-  GB::store(smem + LA::kBytes, rb, tid);
-  __syncthreads();
+  typedef typename Frag<T>::type FragT;
+  FragT fa[2][FM], fb[2][FN];
+  DA da;
+  DB db;
+  da.init(p.a, m0, wave, lane);
+  db.init(p.b, n0, wave, lane);
 
+  // Ring of NS LDS stages.  At the top of iteration kt the stage cur holds
+  // slab kt and the other stages hold (or are loading) slabs kt+1 .. kt+NS-1.
+  // In the last sub-step of iteration kt each wave waits for its part of slab
+  // kt+1, the workgroup synchronises half-way through the MFMAs, the first
+  // fragments of slab kt+1 load, slab kt+NS is issued into stage cur (no wave
+  // reads it any more), and the second half of the MFMAs runs.  Slabs past the
+  // end read out-of-range offsets or unused data and are never consumed, so
+  // the loop body has no data-dependent branches.
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    da.issue(p.a, m0, (int64_t)(kt_begin + st) * BK, smem + st * STAGE, wave, spare);
+    db.issue(p.b, n0, (int64_t)(kt_begin + st) * BK, smem + st * STAGE + DA::kBytes, wave, spare);
+  }
+  wait_vmcnt<(NS - 1) * NIT>();
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa[0][i] = load_frag<T, BM, AK, KB>(smem, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(smem + DA::kBytes, wn * WTN + j * 32, 0, lane);
+
+  int cur = 0;
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int cur = (kt - kt_begin) & 1;
-    const bool more = kt + 1 < kt_end;
-    if (more) {
-      GA::load(ra, p.a, m0, (int64_t)(kt + 1) * BK, tid);
-      GB::load(rb, p.b, n0, (int64_t)(kt + 1) * BK, tid);
-    }
-    const char* sa = smem + cur * STAGE;
-    const char* sb = sa + LA::kBytes;
+    const int nxt = cur + 1 == NS ? 0 : cur + 1;
+    char* sa = smem + cur * STAGE;
+    char* sb = sa + DA::kBytes;
+    char* na = smem + nxt * STAGE;
+    char* nb = na + DA::kBytes;
 #pragma unroll
     for (int kk = 0; kk < SUB; ++kk) {
-      typename Frag<T>::type fa[FM], fb[FN];
+      const int fbuf = kk & 1;
+      if (kk + 1 < SUB) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = load_frag<T, BM, AK>(sa, wm * WTM + i * 32, kk, lane);
+        for (int i = 0; i < FM; ++i) fa[fbuf ^ 1][i] = load_frag<T, BM, AK, KB>(sa, wm * WTM + i * 32, kk + 1, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = load_frag<T, BN, BKM>(sb, wn * WTN + j * 32, kk, lane);
+        for (int j = 0; j < FN; ++j) fb[fbuf ^ 1][j] = load_frag<T, BN, BKM, KB>(sb, wn * WTN + j * 32, kk + 1, lane);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int q = 0; q < NMF; ++q)
+          acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+      } else {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_block(fa[i], fb[j], acc[i][j]);
+        for (int q = 0; q < NMF / 2; ++q)
+          acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+        wait_vmcnt<(NS - 2) * NIT>();
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[0][i] = load_frag<T, BM, AK, KB>(na, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(nb, wn * WTN + j * 32, 0, lane);
+        da.issue(p.a, m0, (int64_t)(kt + NS) * BK, sa, wave, spare);
+        db.issue(p.b, n0, (int64_t)(kt + NS) * BK, sb, wave, spare);
+#pragma unroll
+        for (int q = NMF / 2; q < NMF; ++q)
+          acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+      }
     }
-    if (more) {
-      char* nxt = smem + (cur ^ 1) * STAGE;
-      GA::store(nxt, ra, tid);
-      GB::store(nxt + LA::kBytes, rb, tid);
-    }
-    __syncthreads();
+    cur = nxt;
   }
 
   // ------------------------------------------------------------ epilogues
+  // Lane l, accumulator slot r of block (i, j) holds D[row][col] with
+  // row = mw + 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 and col = nw + 32 j + l % 32.
   const int h = lane >> 5, col = lane & 31;
+  const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
+  const bool full = (mw + WTM <= p.valid_m) && (nw + WTN <= p.valid_n);
   if constexpr (EPI == EPI_LOGITS) {
     // D rows are vocabulary ids (m), columns are tokens (n).  Per token this
     // lane holds 64 of the 128 logits of its wave's slice; its partner lane
     // (lane ^ 32) holds the other 64.
-    const int64_t mw = m0 + wm * WTM;
     const int slice = (int)(mw / 128);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + wn * WTN + j * 32 + col;
+      const int64_t n = nw + j * 32 + col;
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = mw + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (m < p.valid_m) mx = fmaxf(mx, acc[i][j][r]);
+          if (full || m < p.valid_m) mx = fmaxf(mx, acc[i][j][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float s = 0.f;
+      float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = mw + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (m < p.valid_m) s += __expf(acc[i][j][r] - mx);
+          if (full || m < p.valid_m) sum += __expf(acc[i][j][r] - mx);
         }
-      s += __shfl_xor(s, 32);
+      sum += __shfl_xor(sum, 32);
       const bool nvalid = n < p.valid_n;
-      if (h == 0 && nvalid && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, s);
+      if (h == 0 && nvalid && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, sum);
       if (nvalid) {
-        float* zrow = p.out + n * p.ldo;
+        float* zrow = p.out + n * p.ldo + mw + h * 4;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int64_t m = mw + i * 32 + q * 8 + h * 4;
             f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            if (m + 3 < p.valid_m) {
-              *(f32x4*)(zrow + m) = v;
+            const int off = i * 32 + q * 8;
+            if (full || mw + h * 4 + off + 3 < p.valid_m) {
+              *(f32x4*)(zrow + off) = v;
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (m + e < p.valid_m) zrow[m + e] = v[e];
+                if (mw + h * 4 + off + e < p.valid_m) zrow[off + e] = v[e];
             }
           }
       }
     }
   } else {
     float* out = p.out + (EPI == EPI_SLAB ? (int64_t)tc.split * p.split_stride : 0);
+    const bool accum = EPI == EPI_ACCUM && p.beta;
+    const int64_t ldo = p.ldo;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        float* rowbase = out + (mw + i * 32 + h * 4) * ldo + nw + col;
+        if (accum) {
+          // all loads of this row band first, then the adds and stores
+          float old[FN][16];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int64_t n = n0 + wn * WTN + j * 32 + col;
-        if (n >= p.valid_n) continue;
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * WTM + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (m < p.valid_m) {
-            float* dst = out + m * p.ldo + n;
-            if (EPI == EPI_ACCUM && p.beta)
-              *dst += acc[i][j][r];
-            else
-              *dst = acc[i][j][r];
-          }
+            for (int r = 0; r < 16; ++r) old[j][r] = rowbase[((r >> 2) * 8 + (r & 3)) * ldo + j * 32];
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rowbase[((r >> 2) * 8 + (r & 3)) * ldo + j * 32] = old[j][r] + acc[i][j][r];
+        } else {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rowbase[((r >> 2) * 8 + (r & 3)) * ldo + j * 32] = acc[i][j][r];
         }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = nw + j * 32 + col;
+          if (n >= p.valid_n) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t m = mw + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+            if (m < p.valid_m) {
+              float* dst = out + m * ldo + n;
+              *dst = accum ? *dst + acc[i][j][r] : acc[i][j][r];
+            }
+          }
+        }
+    }
   }
 }
 

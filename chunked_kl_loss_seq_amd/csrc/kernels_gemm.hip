@@ -10,11 +10,12 @@ constexpr int kGroupM = 4;
 
 inline int cdiv64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI>
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
 hipError_t run(GemmParams& p, hipStream_t s) {
   const int total = p.tiles_m * p.tiles_n * p.splits;
   const int grid = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI>), dim3(grid), dim3(WM * WN * 64), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI, KB, NS>), dim3(grid), dim3(WM * WN * 64), 0, s,
+                     p);
   return hipGetLastError();
 }
 
@@ -59,8 +60,8 @@ hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int
   p.valid_n = rows;
   p.part = part;
   p.n_slices = n_slices;
-  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, true, true, EPI_LOGITS>(p, s);
-  return run<float, 256, 256, 2, 4, true, true, EPI_LOGITS>(p, s);
+  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
+  return run<float, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
 }
 
 hipError_t launch_dh(Dtype dt, const void* G, int64_t ldg, const void* W, int64_t V, int64_t d, int64_t rows,
@@ -84,11 +85,11 @@ hipError_t launch_dh(Dtype dt, const void* G, int64_t ldg, const void* W, int64_
   p.valid_n = d;
   if (p.splits != splits) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
-    if (bn == 192) return run<__bf16, 256, 192, 4, 2, true, false, EPI_SLAB>(p, s);
-    return run<__bf16, 256, 256, 4, 2, true, false, EPI_SLAB>(p, s);
+    if (bn == 192) return run<__bf16, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
+    return run<__bf16, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
   }
-  if (bn == 192) return run<float, 256, 192, 4, 2, true, false, EPI_SLAB>(p, s);
-  return run<float, 256, 256, 4, 2, true, false, EPI_SLAB>(p, s);
+  if (bn == 192) return run<float, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
+  return run<float, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
 }
 
 hipError_t launch_dw(Dtype dt, const void* G, int64_t ldg, const void* Hc, int64_t V, int64_t d, int64_t rows,
@@ -111,11 +112,11 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t ldg, const void* Hc, int64
   p.valid_n = d;
   p.beta = beta;
   if (dt == DT_BF16) {
-    if (bn == 192) return run<__bf16, 256, 192, 4, 2, false, false, EPI_ACCUM>(p, s);
-    return run<__bf16, 256, 256, 4, 2, false, false, EPI_ACCUM>(p, s);
+    if (bn == 192) return run<__bf16, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
+    return run<__bf16, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
   }
-  if (bn == 192) return run<float, 256, 192, 4, 2, false, false, EPI_ACCUM>(p, s);
-  return run<float, 256, 256, 4, 2, false, false, EPI_ACCUM>(p, s);
+  if (bn == 192) return run<float, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
+  return run<float, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
 }
 
 // ---------------------------------------------------------------- split-K reduce

@@ -243,9 +243,12 @@ def _sampled_full_size(binding, number, n_sample=48):
     assert abs(g["loss"] - mean_kl) <= 1e-5 * abs(mean_kl)
     # dW properties that hold at any size: columns of G sum to zero per row,
     # so the rows of dW sum to zero; and W^T dW = dH^T H (both equal W^T G^T H)
+    # (exact for the oracle; for the GPU, 1^T dW = 1^T (dW - dW_oracle), whose
+    # norm is about ||dW - dW_oracle||_F when the rounding errors are independent,
+    # so the dW tolerance bounds it by 1e-2 ||dW||_F)
     dW = g["dW"].astype(np.float64)
-    col = np.abs(dW.sum(0)).max() / np.abs(dW).max()
-    say(f"[parity {wl.name}] max |sum_v dW[v,:]| / max|dW| = {col:.2e}")
+    col = np.linalg.norm(dW.sum(0)) / np.linalg.norm(dW)
+    say(f"[parity {wl.name}] ||sum_v dW[v,:]|| / ||dW||_F = {col:.2e}")
     assert col <= 1e-2
     U = rng.standard_normal((wl.d, 4))
     lhs = inp["W"].astype(np.float64).T @ (dW @ U)
