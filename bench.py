@@ -87,7 +87,21 @@ def main():
     ap.add_argument("--chunk", type=int, default=-1, help="rows per chunk (default: the workload's own)")
     ap.add_argument("--cpu-rows", type=int, default=256, help="positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 1 << 30, "launches": 5}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",

@@ -119,14 +119,36 @@ __device__ inline void wait_vmcnt() {
 
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past the range: the load returns zeros
 
-// The base is wave-uniform; readfirstlane makes that explicit so the
-// resource lives in SGPRs (otherwise every load gets a waterfall loop).
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + 2 GiB) with raw (unswizzled) addressing.
+// The base is wave-uniform; readfirstlane makes that explicit so the resource
+// lives in SGPRs.
+__device__ inline i32x4 make_rsrc(const void* base) {
   const uint64_t a = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  void* u = (void*)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7FFFFFF0, 0x00020000);
+  i32x4 r;
+  r.x = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  r.y = (int32_t)(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu);  // stride 0
+  r.z = 0x7FFFFFF0;                                                                 // num_records (bytes)
+  r.w = 0x00020000;                                                                 // raw buffer, 32-bit data format
+  return r;
+}
+
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes at byte `voff` of the
+// resource go to LDS byte lds_addr + 16 l (lds_addr is wave-uniform and goes
+// through M0).  Written as inline assembly so that the compiler's wait-count
+// pass, which cannot tell these LDS writes apart from the fragment reads of
+// other stages, does not put a full vmcnt wait in front of every LDS read;
+// the kernel orders them itself with explicit vmcnt waits and barriers.  The
+// instruction has no destination VGPRs.
+__device__ inline void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
 }
 
 // Per-lane state to copy one operand's k-slabs of a tile into LDS.  Lane
@@ -185,7 +207,7 @@ struct SlabDMA {
   // `spare` is 1 KiB of LDS that padding loads may overwrite.
   __device__ inline void issue(const Operand& o, int64_t mn0, int64_t k0, char* lds, int wave, char* spare) const {
     const T* base = (const T*)o.ptr + (KMAJ ? (mn0 * o.ld + k0) : (k0 * o.ld + mn0));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+    const i32x4 rs = make_rsrc(base);
     const bool tail = k0 + kBK > o.k_ext;
     const int kleft = tail ? (int)(o.k_ext - k0) : kBK;  // <= 0 when the slab is past the end
 #pragma unroll
@@ -194,7 +216,7 @@ struct SlabDMA {
       uint32_t v = voff[i];
       if (!real || (tail && (int)kd[i] >= kleft)) v = kOOB;
       char* dst = real ? lds + (i * NW + wave) * 1024 : spare;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, v, 0, 0, 0);
+      dma16(rs, v, lds_addr(dst));
     }
   }
 };
@@ -302,8 +324,11 @@ __device__ inline TileCoord tile_coord(const GemmParams& p) {
 }
 
 // ---------------------------------------------------------------- the kernel
+// At most 256 VGPRs per lane (two waves per SIMD), so that either one 8-wave
+// or two 4-wave workgroups fit a compute unit; with two workgroups their
+// barriers and epilogues overlap each other's MFMA work.
 template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
-__global__ void __launch_bounds__(WM* WN * 64) gemm_kernel(GemmParams p) {
+__global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))) gemm_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int BK = KB / (int)sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;

@@ -105,7 +105,7 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t ldg, const void* Hc, int64
   p.k_tiles = cdiv64(rows, bk);
   p.splits = 1;
   p.k_tiles_per_split = p.k_tiles;
-  p.group_m = kGroupM;
+  p.group_m = 1;  // all d-tiles of a vocabulary row-block together: they share the G^T slab
   p.out = dW;
   p.ldo = d;
   p.valid_m = V;

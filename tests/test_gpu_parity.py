@@ -267,3 +267,8 @@ def test_llama3_head_workload_sampled():
 def test_gpt_oss_head_workload_sampled():
     binding = _need_gpu()
     _sampled_full_size(binding, 4)
+
+
+def test_gpt_oss_head_long_batch_workload_sampled():
+    binding = _need_gpu()
+    _sampled_full_size(binding, 5)
