@@ -25,23 +25,26 @@ inline int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // Device workspace of one call with chunks of C rows.
 struct Layout {
   int64_t C = 0;
-  int64_t ldz = 0;      // fp32 elements per logit row
+  int64_t pblk = 0;     // elements between tile rows of the exp / gradient tiles
   int n_slices = 0;     // (max, sum exp) pairs per row
   int splits = 0;       // k-splits of the dH contraction
-  uint64_t z_off = 0, part_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0, total = 0;
+  uint64_t p_off = 0, part_off = 0, scat_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0, total = 0;
 };
 
-Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t C) {
+Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t esz) {
   Layout L;
   L.C = C;
-  L.ldz = roundup(V, 64);
+  L.pblk = tile_row_stride(V);
   L.n_slices = (int)((V + 127) / 128);
   L.splits = dh_splits(C, d, V);
+  const int64_t tile_rows = (C + 63) / 64;
   uint64_t off = 0;
-  L.z_off = off;
-  off += align256((uint64_t)C * L.ldz * 4);
+  L.p_off = off;
+  off += align256((uint64_t)tile_rows * L.pblk * esz);
   L.part_off = off;
   off += align256((uint64_t)C * L.n_slices * 8);
+  L.scat_off = off;
+  off += align256((uint64_t)C * K * 4);
   L.slab_off = off;
   off += align256((uint64_t)L.splits * C * d * 4);
   L.kl_off = off;
@@ -65,7 +68,7 @@ uint64_t budget_from_env(uint64_t b) {
   return kDefaultBudget;
 }
 
-int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_t budget, Layout* out) {
+int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_t budget, size_t esz, Layout* out) {
   if (N <= 0 || d <= 0 || V <= 0 || K <= 0 || chunk < 0) return CKL_EINVAL;
   if (K > V) return CKL_EINVAL;
   if (d % 8 != 0 || K > kMaxK) return CKL_EUNSUPPORTED;
@@ -73,7 +76,7 @@ int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_
   budget = budget_from_env(budget);
   if (chunk > 0) {
     const int64_t C = chunk < N ? chunk : N;
-    Layout L = make_layout(N, d, V, C);
+    Layout L = make_layout(N, d, V, K, C, esz);
     if (L.total > budget) return CKL_EBUDGET;
     *out = L;
     return CKL_OK;
@@ -81,13 +84,13 @@ int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_
   // largest fitting multiple of 256 rows (or N itself when smaller)
   int64_t cmax = 0;
   if (N <= kRowStep) {
-    if (make_layout(N, d, V, N).total <= budget) cmax = N;
+    if (make_layout(N, d, V, K, N, esz).total <= budget) cmax = N;
   } else {
     int64_t lo = 1, hi = roundup(N, kRowStep) / kRowStep;  // in units of 256 rows
-    if (make_layout(N, d, V, kRowStep).total > budget) return CKL_EBUDGET;
+    if (make_layout(N, d, V, K, kRowStep, esz).total > budget) return CKL_EBUDGET;
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) / 2;
-      if (make_layout(N, d, V, mid * kRowStep).total <= budget)
+      if (make_layout(N, d, V, K, mid * kRowStep, esz).total <= budget)
         lo = mid;
       else
         hi = mid - 1;
@@ -101,7 +104,7 @@ int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_
   int64_t C = roundup((N + nch - 1) / nch, kRowStep);
   if (C > cmax) C = cmax;
   if (C > N) C = N;
-  *out = make_layout(N, d, V, C);
+  *out = make_layout(N, d, V, K, C, esz);
   return CKL_OK;
 }
 
@@ -191,8 +194,9 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
   if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return CKL_EINVAL;
   if (!aligned(ids, 4) || !aligned(tlogit, 4) || !aligned(out_loss, 4)) return CKL_EINVAL;
   if (!aligned(row_kl, 4) || !aligned(row_lse, 4)) return CKL_EINVAL;
+  const size_t esz = dt == DT_BF16 ? 2 : 4;
   Layout L;
-  int st = plan_impl(N, d, V, K, chunk, 0, &L);
+  int st = plan_impl(N, d, V, K, chunk, 0, esz, &L);
   if (st != CKL_OK) return st;
   if ((N + L.C - 1) / L.C > (int64_t)1 << 24) return CKL_EUNSUPPORTED;
 
@@ -202,14 +206,13 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
   st = get_workspace(dev, stream, L.total, &ws);
   if (st != CKL_OK) return st;
   char* base = (char*)ws;
-  float* Z = (float*)(base + L.z_off);
+  void* P = base + L.p_off;
   float2* part = (float2*)(base + L.part_off);
+  float* scat = (float*)(base + L.scat_off);
   float* slab = (float*)(base + L.slab_off);
   float* kl = row_kl ? row_kl : (float*)(base + L.kl_off);
   float* lse = row_lse ? row_lse : (float*)(base + L.lse_off);
   void* scal = base + L.scal_off;
-  const size_t esz = dt == DT_BF16 ? 2 : 4;
-  const int64_t ldg = dt == DT_BF16 ? 2 * L.ldz : L.ldz;
 
   {
     Timed t(T_OTHER, stream);
@@ -220,12 +223,12 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
     const void* Hc = (const char*)H + (size_t)r0 * d * esz;
     {
       Timed t(T_LOGITS, stream);
-      CKL_TRY(launch_logits(dt, W, Hc, V, d, rows, Z, L.ldz, part, L.n_slices, stream));
+      CKL_TRY(launch_logits(dt, W, Hc, V, d, rows, P, L.pblk, part, L.n_slices, stream));
     }
     {
       RowArgs a{};
-      a.Z = Z;
-      a.ldz = L.ldz;
+      a.P = P;
+      a.pblk = L.pblk;
       a.part = part;
       a.n_slices = L.n_slices;
       a.ids = ids + r0 * K;
@@ -235,17 +238,20 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
       a.V = V;
       a.K = (int)K;
       a.rows = rows;
+      a.scat = scat;
       a.kl_out = kl + r0;
       a.lse_out = lse + r0;
       Timed t(T_ROWS, stream);
-      CKL_TRY(launch_rows(dt, a, stream));
+      CKL_TRY(launch_row_stats(dt, a, stream));
+      CKL_TRY(launch_dense(dt, a, stream));
+      CKL_TRY(launch_scatter(dt, a, stream));
     }
     int splits = dh_splits(rows, d, V);
     const int64_t cap = (int64_t)L.splits * L.C / rows;  // slab capacity in splits of this chunk
     if (splits > cap) splits = (int)cap;
     {
       Timed t(T_DH, stream);
-      CKL_TRY(launch_dh(dt, Z, ldg, W, V, d, rows, slab, splits, stream));
+      CKL_TRY(launch_dh(dt, P, L.pblk, W, V, d, rows, slab, splits, stream));
     }
     {
       Timed t(T_DHRED, stream);
@@ -253,7 +259,7 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
     }
     {
       Timed t(T_DW, stream);
-      CKL_TRY(launch_dw(dt, Z, ldg, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, stream));
+      CKL_TRY(launch_dw(dt, P, L.pblk, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, stream));
     }
   }
   {
@@ -306,7 +312,7 @@ int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chun
   if (dtype != CKL_DTYPE_BF16 && dtype != CKL_DTYPE_F32) return CKL_EINVAL;
   try {
     Layout L;
-    const int st = plan_impl(N, d, V, K, chunk, budget_bytes, &L);
+    const int st = plan_impl(N, d, V, K, chunk, budget_bytes, dtype == CKL_DTYPE_BF16 ? 2 : 4, &L);
     if (st != CKL_OK) return st;
     if (chunk_out) *chunk_out = L.C;
     if (workspace_bytes_out) *workspace_bytes_out = L.total;
@@ -358,21 +364,25 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
     if (R <= 0 || V <= 0 || K <= 0 || K > V) return CKL_EINVAL;
     if (K > kMaxK) return CKL_EUNSUPPORTED;
     if (R > (int64_t)1 << 20 || V > (int64_t)1 << 30) return CKL_EUNSUPPORTED;
-    const int64_t ldz = roundup(V, 64);
+    const Dtype gdt = g_bf16 ? DT_BF16 : DT_F32;
+    const size_t esz = g_bf16 ? 2 : 4;
+    const int64_t pblk = tile_row_stride(V);
     const int n_slices = (int)((V + 127) / 128);
-    const uint64_t zb = align256((uint64_t)R * ldz * 4), pb = align256((uint64_t)R * n_slices * 8);
+    const uint64_t pb = align256((uint64_t)((R + 63) / 64) * pblk * esz);
+    const uint64_t qb = align256((uint64_t)R * n_slices * 8);
+    const uint64_t sb = align256((uint64_t)R * K * 4);
     int dev = 0;
     CKL_TRY(hipGetDevice(&dev));
     void* ws = nullptr;
-    int st = get_workspace(dev, stream, zb + pb, &ws);
+    int st = get_workspace(dev, stream, pb + qb + sb, &ws);
     if (st != CKL_OK) return st;
-    float* Zw = (float*)ws;
-    float2* part = (float2*)((char*)ws + zb);
-    CKL_TRY(hipMemcpy2DAsync(Zw, ldz * 4, Z, V * 4, V * 4, R, hipMemcpyDeviceToDevice, stream));
-    CKL_TRY(launch_partials_from_z(Zw, ldz, R, V, part, n_slices, stream));
+    void* P = ws;
+    float2* part = (float2*)((char*)ws + pb);
+    float* scat = (float*)((char*)ws + pb + qb);
+    CKL_TRY(launch_partials_from_z(gdt, Z, V, R, V, part, n_slices, P, pblk, stream));
     RowArgs a{};
-    a.Z = Zw;
-    a.ldz = ldz;
+    a.P = P;
+    a.pblk = pblk;
     a.part = part;
     a.n_slices = n_slices;
     a.ids = idx;
@@ -383,13 +393,15 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
     a.V = V;
     a.K = (int)K;
     a.rows = R;
+    a.scat = scat;
     a.kl_out = kl_out;
     a.lse_out = lse_out;
     a.zg_dbg = zg_out;
     a.sid_dbg = scatter_ids_out;
-    CKL_TRY(launch_rows(g_bf16 ? DT_BF16 : DT_F32, a, stream));
-    const size_t esz = g_bf16 ? 2 : 4;
-    CKL_TRY(hipMemcpy2DAsync(G_out, V * esz, Zw, ldz * 4, V * esz, R, hipMemcpyDeviceToDevice, stream));
+    CKL_TRY(launch_row_stats(gdt, a, stream));
+    CKL_TRY(launch_dense(gdt, a, stream));
+    CKL_TRY(launch_scatter(gdt, a, stream));
+    CKL_TRY(launch_untile(gdt, P, pblk, R, V, G_out, stream));
     CKL_TRY(hipStreamSynchronize(stream));
     return CKL_OK;
   } catch (...) {

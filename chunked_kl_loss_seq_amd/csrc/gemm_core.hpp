@@ -41,18 +41,28 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// One GEMM operand in global memory.  Element (mn, k) lives at
-// ptr[mn * ld + k] when k-major and at ptr[k * ld + mn] when mn-major.
-// Rows mn >= mn_ext and columns k >= k_ext read as zero.
+// One GEMM operand in global memory, stored as rows of a row-major matrix:
+// a k-major operand has storage row = mn and column = k, an mn-major one
+// storage row = k and column = mn.  Element (row, col) lives at
+//   ptr[row * ld + col]                                        (blk == 0), or
+//   ptr[(row / 64) * blk + (col / 64) * 4096 + (row % 64) * 64 + col % 64]
+// in the tiled layout of 64 x 64 element tiles (blk = elements between two
+// tile rows).  Rows mn >= mn_ext and columns k >= k_ext read as zero.
 struct Operand {
   const void* ptr;
   int64_t ld;
   int64_t mn_ext;
   int64_t k_ext;
+  int64_t blk;
 };
 
+__device__ inline int64_t elem_offset(const Operand& o, int64_t row, int64_t col) {
+  if (o.blk == 0) return row * o.ld + col;
+  return (row >> 6) * o.blk + (col >> 6) * 4096 + (row & 63) * 64 + (col & 63);
+}
+
 enum EpilogueKind : int {
-  EPI_LOGITS = 0,  // Z[n][m] = D[m][n] (fp32) + per (n, 128-row slice of m) (max, sum exp)
+  EPI_LOGITS = 0,  // per (n, 128-row slice of m): mx = max D, P[n][m] = exp(D[m][n] - mx), (mx, sum P)
   EPI_SLAB = 1,    // out[m][n] = D[m][n] (fp32), one slab per k-split
   EPI_ACCUM = 2,   // out[m][n] = D[m][n] (beta = 0) or out[m][n] += D[m][n] (beta = 1)
 };
@@ -64,8 +74,8 @@ struct GemmParams {
   int splits;            // k-splits; each covers k_tiles_per_split k-steps
   int k_tiles_per_split;
   int group_m;           // m-tiles per group in the tile order
-  float* out;            // Z, slab base or dW
-  int64_t ldo;
+  void* out;             // EPI_LOGITS: exp values (tiled, element type T); else fp32 slab base or dW
+  int64_t ldo;           // EPI_LOGITS: elements between tile rows of out; else row stride
   int64_t split_stride;  // elements between k-split slabs (EPI_SLAB)
   int64_t valid_m, valid_n;  // stores are limited to m < valid_m, n < valid_n
   float2* part;          // EPI_LOGITS: partial (max, sum exp) per [n][slice]
@@ -174,11 +184,20 @@ struct SlabDMA {
   __device__ static inline bool has(int wave, int i) { return kEven || i * NW + wave < kBlocks; }
   static constexpr int kSpare = kEven ? 0 : 1024;  // LDS bytes for the padding loads
 
+  // Lane offsets relative to the slab origin.  The origin (row0, col0) of
+  // every slab of a tile has row0 and col0 aligned to the tile (64 elements)
+  // along mn and to the slab depth along k, and a slab never crosses a
+  // 64-element tile boundary along k, so these offsets are the same for all
+  // slabs of the tile in both layouts.
   __device__ inline void init(const Operand& o, int64_t mn0, int wave, int lane) {
+    // representative origin: k0 = 0
+    const int64_t r0 = KMAJ ? mn0 : 0, c0 = KMAJ ? 0 : mn0;
+    const int64_t base = elem_offset(o, r0, c0);
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const int b = i * NW + wave;
       int row_mn, kdel;
+      int64_t e;
       if (KMAJ) {
         typedef KTile<R, KB> L;
         const int q = b * 1024 + lane * 16;
@@ -187,7 +206,7 @@ struct SlabDMA {
         const int c = pc ^ ((row / L::kRowsPerBankRow) % L::kCPR);
         row_mn = row;
         kdel = c * kEPC;
-        voff[i] = (uint32_t)((int64_t)row * o.ld * (int64_t)sizeof(T) + c * 16);
+        e = elem_offset(o, r0 + row, c0 + kdel) - base;
       } else {
         typedef MNTile<T, R, kBK> L;
         const int q = b * 1024 + lane * 16;
@@ -196,8 +215,9 @@ struct SlabDMA {
         const int lb = (((pb >> 6) ^ L::swz(krow)) << 6) | (pb & 63);
         row_mn = lb / (int)sizeof(T);
         kdel = krow;
-        voff[i] = (uint32_t)((int64_t)krow * o.ld * (int64_t)sizeof(T) + lb);
+        e = elem_offset(o, r0 + krow, c0 + row_mn) - base;
       }
+      voff[i] = (uint32_t)(e * (int64_t)sizeof(T));
       kd[i] = (uint8_t)kdel;
       if (mn0 + row_mn >= o.mn_ext) voff[i] = kOOB;
     }
@@ -206,7 +226,7 @@ struct SlabDMA {
   // Issue the copy of slab origin k0 into `lds` (a wave-uniform LDS address);
   // `spare` is 1 KiB of LDS that padding loads may overwrite.
   __device__ inline void issue(const Operand& o, int64_t mn0, int64_t k0, char* lds, int wave, char* spare) const {
-    const T* base = (const T*)o.ptr + (KMAJ ? (mn0 * o.ld + k0) : (k0 * o.ld + mn0));
+    const T* base = (const T*)o.ptr + (KMAJ ? elem_offset(o, mn0, k0) : elem_offset(o, k0, mn0));
     const i32x4 rs = make_rsrc(base);
     const bool tail = k0 + kBK > o.k_ext;
     const int kleft = tail ? (int)(o.k_ext - k0) : kBK;  // <= 0 when the slab is past the end
@@ -438,8 +458,11 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   if constexpr (EPI == EPI_LOGITS) {
     // D rows are vocabulary ids (m), columns are tokens (n).  Per token this
     // lane holds 64 of the 128 logits of its wave's slice; its partner lane
-    // (lane ^ 32) holds the other 64.
+    // (lane ^ 32) holds the other 64.  The slice max mx, the exp values
+    // P = exp(z - mx) (stored in the tiled layout, element type T) and their
+    // fp32 sum are what the row pass needs; the logits themselves are not kept.
     const int slice = (int)(mw / 128);
+    T* pout = (T*)p.out;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = nw + j * 32 + col;
@@ -458,31 +481,38 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = mw + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (full || m < p.valid_m) sum += __expf(acc[i][j][r] - mx);
+          const float e = __expf(acc[i][j][r] - mx);
+          acc[i][j][r] = e;
+          if (full || m < p.valid_m) sum += e;
         }
       sum += __shfl_xor(sum, 32);
       const bool nvalid = n < p.valid_n;
       if (h == 0 && nvalid && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, sum);
       if (nvalid) {
-        float* zrow = p.out + n * p.ldo + mw + h * 4;
+        // tile row of token n; the 4 values of (i, q) are consecutive ids
+        T* prow = pout + (n >> 6) * p.ldo + (n & 63) * 64;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            const int off = i * 32 + q * 8;
-            if (full || mw + h * 4 + off + 3 < p.valid_m) {
-              *(f32x4*)(zrow + off) = v;
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (mw + h * 4 + off + e < p.valid_m) zrow[off + e] = v[e];
+            const int64_t m = mw + i * 32 + q * 8 + h * 4;
+            if (full || m < p.valid_m) {
+              T* dst = prow + (m >> 6) * 4096 + (m & 63);
+              if constexpr (sizeof(T) == 2) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                bf16x4 v = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
+                            (__bf16)acc[i][j][4 * q + 3]};
+                *(bf16x4*)dst = v;
+              } else {
+                f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                *(f32x4*)dst = v;
+              }
             }
           }
       }
     }
   } else {
-    float* out = p.out + (EPI == EPI_SLAB ? (int64_t)tc.split * p.split_stride : 0);
+    float* out = (float*)p.out + (EPI == EPI_SLAB ? (int64_t)tc.split * p.split_stride : 0);
     const bool accum = EPI == EPI_ACCUM && p.beta;
     const int64_t ldo = p.ldo;
     if (full) {

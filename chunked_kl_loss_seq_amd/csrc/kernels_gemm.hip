@@ -42,11 +42,11 @@ int dh_splits(int64_t rows, int64_t d, int64_t V) {
   return best;
 }
 
-hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int64_t d, int64_t rows,
-                         float* Z, int64_t ldz, float2* part, int n_slices, hipStream_t s) {
+hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
+                         int64_t pblk, float2* part, int n_slices, hipStream_t s) {
   GemmParams p{};
-  p.a = Operand{W, d, V, d};
-  p.b = Operand{Hc, d, rows, d};
+  p.a = Operand{W, d, V, d, 0};
+  p.b = Operand{Hc, d, rows, d, 0};
   p.tiles_m = cdiv64(V, 256);
   p.tiles_n = cdiv64(rows, 256);
   const int bk = dt == DT_BF16 ? 64 : 32;
@@ -54,8 +54,8 @@ hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int
   p.splits = 1;
   p.k_tiles_per_split = p.k_tiles;
   p.group_m = kGroupM;
-  p.out = Z;
-  p.ldo = ldz;
+  p.out = P;
+  p.ldo = pblk;
   p.valid_m = V;
   p.valid_n = rows;
   p.part = part;
@@ -64,14 +64,13 @@ hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int
   return run<float, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
 }
 
-hipError_t launch_dh(Dtype dt, const void* G, int64_t ldg, const void* W, int64_t V, int64_t d, int64_t rows,
+hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* W, int64_t V, int64_t d, int64_t rows,
                      float* slab, int splits, hipStream_t s) {
-  const int64_t vpad = (V + 7) / 8 * 8;
   const int bn = d_tile(d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
-  p.a = Operand{G, ldg, rows, vpad};
-  p.b = Operand{W, d, d, V};
+  p.a = Operand{G, 0, rows, V, gblk};  // tiled: storage row = token, column = vocabulary id
+  p.b = Operand{W, d, d, V, 0};        // storage row = vocabulary id (k), column = d (n)
   p.tiles_m = cdiv64(rows, 256);
   p.tiles_n = cdiv64(d, bn);
   p.k_tiles = cdiv64(V, bk);
@@ -92,14 +91,13 @@ hipError_t launch_dh(Dtype dt, const void* G, int64_t ldg, const void* W, int64_
   return run<float, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
 }
 
-hipError_t launch_dw(Dtype dt, const void* G, int64_t ldg, const void* Hc, int64_t V, int64_t d, int64_t rows,
+hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int64_t V, int64_t d, int64_t rows,
                      float* dW, int beta, hipStream_t s) {
-  const int64_t vpad = (V + 7) / 8 * 8;
   const int bn = d_tile(d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
-  p.a = Operand{G, ldg, vpad, rows};
-  p.b = Operand{Hc, d, d, rows};
+  p.a = Operand{G, 0, V, rows, gblk};  // tiled: storage row = token (k), column = vocabulary id (m)
+  p.b = Operand{Hc, d, d, rows, 0};
   p.tiles_m = cdiv64(V, 256);
   p.tiles_n = cdiv64(d, bn);
   p.k_tiles = cdiv64(rows, bk);

@@ -1,7 +1,7 @@
 // Per-token kernels of the fused chunked KL loss: valid-token count, the row
-// pass over a chunk of logits (log-normaliser, teacher softmax over the cached
-// top-K, gather, KL, in-place logit gradient and top-K scatter) and the final
-// loss reduction.
+// pass over a chunk (log-normaliser, teacher softmax over the cached top-K,
+// gather, KL, in-place logit gradient and top-K scatter) and the final loss
+// reduction.
 //
 // Definitions followed (the pages print no formulas; these are the plain
 // readings that the rest of the pages support):
@@ -13,6 +13,17 @@
 //    sequence grid of section "Why is this so hard to do cheaply?";
 //  * loss = mean over valid positions of KL(p_T || p_S); its logit gradient is
 //    w_r (softmax(z_r) - scatter(p_T,r)) with w_r = mask_r / n_valid.
+//
+// Chunk workspace.  The logits GEMM leaves, per token r and 128-id slice s,
+// the slice max m_rs and the sum of exp(z - m_rs) (the "slice pairs"), and per
+// logit the value p = exp(z - m_rs) in the element type T of the gradient,
+// laid out in 64 x 64 tiles (tile_off below).  Then, for each chunk:
+//  1. row_stats: lse_r = merge of the slice pairs; teacher softmax; the cached
+//     ids' logits z = m_rs + log p; KL_r; the per-slice gradient factor
+//     f_rs = w_r exp(m_rs - lse_r) (written over the pair's sum); and the exact
+//     gradient value at each cached id, f_rs p - w_r p_T;
+//  2. dense: G = f_rs p over every tile, in place (same element, same type);
+//  3. scatter: G at the cached ids <- the exact values of step 1.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -33,6 +44,12 @@ struct Scalars {
   float scale;
   float pad;
 };
+
+// Element (row r, column v) of a 64 x 64-tiled matrix whose tile rows are
+// `blk` elements apart.
+__device__ inline int64_t tile_off(int64_t r, int64_t v, int64_t blk) {
+  return (r >> 6) * blk + (v >> 6) * 4096 + (r & 63) * 64 + (v & 63);
+}
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -104,9 +121,10 @@ __device__ inline void block_lse_merge(float& m, float& s, float* red) {
   for (int i = 1; i < NT / 64; ++i) lse_merge(m, s, red[2 * i], red[2 * i + 1]);
 }
 
-// Make every global access this thread issued complete before the barrier
-// that follows, so that other waves may overwrite those bytes after it.
-__device__ inline void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
+template <typename T>
+__device__ inline float to_f(T x) {
+  return (float)x;
+}
 
 // ------------------------------------------------------------------ valid count
 __global__ void __launch_bounds__(1024) mask_count_kernel(const uint8_t* __restrict__ mask, int64_t N,
@@ -131,28 +149,22 @@ __global__ void __launch_bounds__(1024) mask_count_kernel(const uint8_t* __restr
   }
 }
 
-// ------------------------------------------------------------------ row pass
-// One workgroup per token row.  In the bf16 form the gradient row (bf16) is
-// written over the first half of the bytes of its own fp32 logit row.  The row
-// is walked in segments of 2048 logits: every thread reads its 8 logits of a
-// segment and converts them, the workgroup synchronises, and only then are
-// the 16-byte gradient pieces of that segment stored; they overwrite logits of
-// earlier or the same segment only, all of which have been read.
-template <bool G_BF16>
-__global__ void __launch_bounds__(kRowThreads) row_kernel(RowArgs a) {
+// ------------------------------------------------------------------ 1. row statistics
+// One workgroup per token row.
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
   constexpr int NT = kRowThreads;
   __shared__ float red[2 * (NT / 64)];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  float* zrow = a.Z + r * a.ldz;
   const Scalars* sc = (const Scalars*)a.scal;
   const float scale = sc ? sc->scale : a.scale_value;
   const bool valid = a.mask == nullptr || a.mask[r] != 0;
   const float w = valid ? scale : 0.f;
+  float2* prow = a.part + r * a.n_slices;
 
-  // student log-normaliser from the per-slice partials
+  // student log-normaliser from the slice pairs
   float m = -INFINITY, s = 0.f;
-  const float2* prow = a.part + r * a.n_slices;
   for (int p = tid; p < a.n_slices; p += NT) {
     const float2 q = prow[p];
     lse_merge(m, s, q.x, q.y);
@@ -160,9 +172,10 @@ __global__ void __launch_bounds__(kRowThreads) row_kernel(RowArgs a) {
   block_lse_merge<NT>(m, s, red);
   const float lse = m + logf(s);
 
-  // teacher softmax over the cached logits, gather, KL, scatter values
+  // teacher softmax over the cached logits; gather; KL; exact values at the ids
+  const T* P = (const T*)a.P;
   const int K = a.K;
-  float tv[kKPT], gv[kKPT];
+  float tv[kKPT];
   int iv[kKPT];
   float tmax = -INFINITY;
 #pragma unroll
@@ -186,82 +199,30 @@ __global__ void __launch_bounds__(kRowThreads) row_kernel(RowArgs a) {
 #pragma unroll
   for (int q = 0; q < kKPT; ++q) {
     const int k = tid + q * NT;
-    gv[q] = 0.f;
     if (k < K) {
+      const int id = iv[q];
+      const float ms = prow[id >> 7].x;
+      const float pv = to_f(P[tile_off(r, id, a.pblk)]);
+      // z = m + log p; a p that underflowed to zero (z more than ~103 below
+      // its slice max) is read as the smallest positive float
+      const float zg = ms + logf(fmaxf(pv, 1.4e-45f));
       const float lpt = tv[q] - lse_t;
       const float pt = __expf(lpt);
-      const float zg = zrow[iv[q]];
       klp += pt * (lpt - (zg - lse));
-      gv[q] = valid ? w * (__expf(zg - lse) - pt) : 0.f;
+      a.scat[r * K + k] = valid ? w * __expf(ms - lse) * pv - w * pt : 0.f;
       if (a.zg_dbg) {
         a.zg_dbg[r * K + k] = zg;
-        a.sid_dbg[r * K + k] = iv[q];
+        a.sid_dbg[r * K + k] = id;
       }
     }
   }
   const float kl = block_sum<NT>(klp, red);
-  drain_memory();
-  __syncthreads();
 
-  // dense gradient pass, in place
-  const int64_t V = a.V;
-  const int64_t vpad = (V + 7) / 8 * 8;
-  if constexpr (G_BF16) {
-    typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-    __bf16* grow = (__bf16*)zrow;
-    const int64_t nseg = (vpad + 8 * NT - 1) / (8 * NT);
-    f32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-    int64_t j = (int64_t)tid * 8;
-    if (valid && j < V) {
-      x0 = *(const f32x4*)(zrow + j);
-      x1 = *(const f32x4*)(zrow + j + 4);
-    }
-    for (int64_t sg = 0; sg < nseg; ++sg) {
-      j = sg * 8 * NT + (int64_t)tid * 8;
-      bf16x8 g;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float z = e < 4 ? x0[e] : x1[e - 4];
-        const float v = (valid && j + e < V) ? w * __expf(z - lse) : 0.f;
-        g[e] = (__bf16)v;
-      }
-      const int64_t jn = j + 8 * NT;
-      if (valid && sg + 1 < nseg && jn < V) {
-        x0 = *(const f32x4*)(zrow + jn);
-        x1 = *(const f32x4*)(zrow + jn + 4);
-      }
-      // The converted values must exist (so this segment's logits have been
-      // read) before the barrier; the next segment's loads may stay in flight,
-      // their bytes are not stored to before the next barrier.
-      u32x4 gbits = __builtin_bit_cast(u32x4, g);
-      asm volatile("" ::"v"(gbits.x), "v"(gbits.y), "v"(gbits.z), "v"(gbits.w));
-      __syncthreads();
-      if (j < vpad) *(u32x4*)(grow + j) = gbits;
-    }
-  } else {
-    for (int64_t j = (int64_t)tid * 4; j < vpad; j += 4 * NT) {
-      f32x4 x = {0, 0, 0, 0};
-      if (valid && j < V) x = *(const f32x4*)(zrow + j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (valid && j + e < V) ? w * __expf(x[e] - lse) : 0.f;
-      *(f32x4*)(zrow + j) = x;
-    }
-  }
-  drain_memory();
+  // every thread has read the pairs it needs; now the factors replace the sums
   __syncthreads();
-
-  // the cached ids get the exact combined value w (p_S - p_T)
-  if (valid) {
-#pragma unroll
-    for (int q = 0; q < kKPT; ++q) {
-      const int k = tid + q * NT;
-      if (k < K) {
-        if constexpr (G_BF16)
-          ((__bf16*)zrow)[iv[q]] = (__bf16)gv[q];
-        else
-          zrow[iv[q]] = gv[q];
-      }
-    }
+  for (int p = tid; p < a.n_slices; p += NT) {
+    const float2 q = prow[p];
+    prow[p].y = valid ? w * __expf(q.x - lse) : 0.f;
   }
   if (tid == 0) {
     a.kl_out[r] = valid ? kl : 0.f;
@@ -269,9 +230,60 @@ __global__ void __launch_bounds__(kRowThreads) row_kernel(RowArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ debug partials
+// ------------------------------------------------------------------ 2. dense gradient
+// One workgroup per 64 x 64 tile: thread t owns row t / 4, columns
+// 16 (t % 4) .. + 15.  G = f p in place; zero for ids >= V and rows >= rows.
+template <typename T>
+__global__ void __launch_bounds__(256) dense_kernel(RowArgs a) {
+  const int64_t tb = blockIdx.y, vb = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t r = tb * 64 + (tid >> 2);
+  const int64_t v0 = vb * 64 + (tid & 3) * 16;
+  T* g = (T*)a.P + tile_off(r, v0, a.pblk);
+  // rows past the chunk hold no exp values (possibly not even numbers): they
+  // are written as zeros without being read into the product
+  const bool row_ok = r < a.rows;
+  float f = 0.f;
+  if (row_ok && v0 < a.V) f = a.part[r * a.n_slices + (v0 >> 7)].y;
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 x = *(const bf16x8*)(g + 8 * h);
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (__bf16)((row_ok && v0 + 8 * h + e < a.V) ? f * (float)x[e] : 0.f);
+      *(bf16x8*)(g + 8 * h) = y;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      f32x4 x = *(const f32x4*)(g + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (row_ok && v0 + 4 * h + e < a.V) ? f * x[e] : 0.f;
+      *(f32x4*)(g + 4 * h) = x;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 3. top-K scatter
+template <typename T>
+__global__ void __launch_bounds__(256) scatter_kernel(RowArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.rows * a.K) return;
+  const int64_t r = i / a.K;
+  if (a.mask != nullptr && a.mask[r] == 0) return;
+  const int id = a.ids[i];
+  ((T*)a.P)[tile_off(r, id, a.pblk)] = (T)a.scat[i];
+}
+
+// ------------------------------------------------------------------ debug helpers
+// Slice pairs and exp values of caller-given fp32 logits (the same quantities
+// the logits GEMM leaves), one workgroup per (128-id slice, row).
+template <typename T>
 __global__ void __launch_bounds__(128) partials_from_z_kernel(const float* __restrict__ Z, int64_t ldz, int64_t V,
-                                                              float2* __restrict__ part, int n_slices) {
+                                                              float2* __restrict__ part, int n_slices, T* P,
+                                                              int64_t pblk) {
   __shared__ float red[4];
   const int64_t r = blockIdx.y;
   const int slice = blockIdx.x;
@@ -283,10 +295,21 @@ __global__ void __launch_bounds__(128) partials_from_z_kernel(const float* __res
   __syncthreads();
   m = fmaxf(red[0], red[1]);
   __syncthreads();
-  float s = wave_sum(ok ? __expf(z - m) : 0.f);
+  const float e = ok ? __expf(z - m) : 0.f;
+  if (ok) P[tile_off(r, j, pblk)] = (T)e;
+  float s = wave_sum(e);
   if ((threadIdx.x & 63) == 0) red[2 + (threadIdx.x >> 6)] = s;
   __syncthreads();
   if (threadIdx.x == 0) part[r * n_slices + slice] = make_float2(m, red[2] + red[3]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) untile_kernel(const T* __restrict__ P, int64_t pblk, int64_t R, int64_t V,
+                                                     T* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * V) return;
+  const int64_t r = i / V, v = i - r * V;
+  out[i] = P[tile_off(r, v, pblk)];
 }
 
 // ------------------------------------------------------------------ finalize
@@ -314,20 +337,60 @@ hipError_t launch_mask_count(const uint8_t* mask, int64_t N, void* scal, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_rows(Dtype g_dt, const RowArgs& a, hipStream_t s) {
+hipError_t launch_row_stats(Dtype g_dt, const RowArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (g_dt == DT_BF16)
-    hipLaunchKernelGGL(row_kernel<true>, dim3((unsigned)a.rows), dim3(kRowThreads), 0, s, a);
+    hipLaunchKernelGGL(row_stats_kernel<__bf16>, dim3((unsigned)a.rows), dim3(kRowThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(row_kernel<false>, dim3((unsigned)a.rows), dim3(kRowThreads), 0, s, a);
+    hipLaunchKernelGGL(row_stats_kernel<float>, dim3((unsigned)a.rows), dim3(kRowThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_partials_from_z(const float* Z, int64_t ldz, int64_t rows, int64_t V, float2* part,
-                                  int n_slices, hipStream_t s) {
+hipError_t launch_dense(Dtype g_dt, const RowArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.V + 63) / 64), (unsigned)((a.rows + 63) / 64));
+  if (g_dt == DT_BF16)
+    hipLaunchKernelGGL(dense_kernel<__bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(dense_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(Dtype g_dt, const RowArgs& a, hipStream_t s) {
+  const int64_t n = a.rows * a.K;
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (g_dt == DT_BF16)
+    hipLaunchKernelGGL(scatter_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(scatter_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_partials_from_z(Dtype g_dt, const float* Z, int64_t ldz, int64_t rows, int64_t V, float2* part,
+                                  int n_slices, void* P, int64_t pblk, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(partials_from_z_kernel, dim3(n_slices, (unsigned)rows), dim3(128), 0, s, Z, ldz, V, part,
-                     n_slices);
+  const dim3 grid(n_slices, (unsigned)rows);
+  if (g_dt == DT_BF16)
+    hipLaunchKernelGGL(partials_from_z_kernel<__bf16>, grid, dim3(128), 0, s, Z, ldz, V, part, n_slices,
+                       (__bf16*)P, pblk);
+  else
+    hipLaunchKernelGGL(partials_from_z_kernel<float>, grid, dim3(128), 0, s, Z, ldz, V, part, n_slices, (float*)P,
+                       pblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_untile(Dtype g_dt, const void* P, int64_t pblk, int64_t rows, int64_t V, void* out,
+                         hipStream_t s) {
+  const int64_t n = rows * V;
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (g_dt == DT_BF16)
+    hipLaunchKernelGGL(untile_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, (const __bf16*)P, pblk, rows, V,
+                       (__bf16*)out);
+  else
+    hipLaunchKernelGGL(untile_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)P, pblk, rows, V,
+                       (float*)out);
   return hipGetLastError();
 }
 

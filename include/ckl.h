@@ -119,8 +119,10 @@ const char* ckl_strerror(int status);
 /* Test entry: the row pass alone on caller-given fp32 logits Z [R, V]
  * (row stride V): log-normaliser, teacher softmax, gather, KL and the logit
  * gradient with weight `scale` for rows whose mask is 1 (or all rows if mask
- * is NULL).  Outputs (device, caller-owned):
- *   zg_out          fp32 [R, K]  the logits gathered at the teacher ids
+ * is NULL).  Z is first turned into what the logits GEMM leaves in the
+ * workspace (per 128-id slice: max m and exp(z - m) in the gradient's element
+ * type), then the production row kernels run.  Outputs (device, caller-owned):
+ *   zg_out          fp32 [R, K]  the logits at the teacher ids, rebuilt as m + log exp(z - m)
  *   scatter_ids_out int32 [R, K] the ids the top-K values were scattered to
  *   G_out           [R, V]       gradient, bf16 if g_bf16 else fp32
  *   kl_out, lse_out fp32 [R]     per-row KL (0 for masked rows) and logsumexp

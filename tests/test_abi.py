@@ -35,11 +35,13 @@ def test_strerror():
 GiB = 1 << 30
 
 
-def ws_formula(N, d, V, C, splits):
+def ws_formula(N, d, V, K, C, splits, esz=2):
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    ldz = (V + 63) // 64 * 64
-    nsl = (V + 127) // 128
-    return a(C * ldz * 4) + a(C * nsl * 8) + a(splits * C * d * 4) + 2 * a(N * 4) + 256
+    pblk = -(-V // 64) * 4096          # elements between 64-row tile rows of the exp / gradient tiles
+    tile_rows = -(-C // 64)
+    nsl = -(-V // 128)
+    return (a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
+            + 2 * a(N * 4) + 256)
 
 
 def test_plan_explicit_chunk_matches_formula():
@@ -47,7 +49,9 @@ def test_plan_explicit_chunk_matches_formula():
         c, ws = B.plan(N, d, V, K, chunk=C)
         assert c == min(C, N)
         # the dH split count is 1..8; the bytes must match the formula for one of them
-        assert any(ws == ws_formula(N, d, V, c, s) for s in range(1, 9)), (N, d, V, ws)
+        assert any(ws == ws_formula(N, d, V, K, c, s) for s in range(1, 9)), (N, d, V, ws)
+    c, ws = B.plan(256, 256, 4096, 16, dtype="f32", chunk=64)
+    assert any(ws == ws_formula(256, 256, 4096, 16, 64, s, esz=4) for s in range(1, 9))
 
 
 def test_plan_gpt_oss_head_fits_six_gib():
@@ -72,7 +76,7 @@ def test_plan_workspace_bounded_in_sequence_length():
         n_chunks = -(-N // c)
         assert n_chunks >= prev_chunks
         prev_chunks = n_chunks
-    assert prev_chunks >= 262144 // 8192
+    assert prev_chunks >= 262144 // 16384
 
 
 def test_plan_budget_errors():
@@ -80,7 +84,7 @@ def test_plan_budget_errors():
         B.plan(32768, 2880, 201088, 100, budget_bytes=100 << 20)
     assert e.value.status == -3
     with pytest.raises(B.CklError) as e:
-        B.plan(32768, 2880, 201088, 100, chunk=16384)  # 16384 x 201088 x 4 B > 6 GiB
+        B.plan(32768, 2880, 201088, 100, chunk=16384)  # 16384 x 201088 x 2 B + slabs > 6 GiB
     assert e.value.status == -3
 
 
