@@ -28,7 +28,8 @@ struct Layout {
   int64_t pblk = 0;     // elements between tile rows of the exp / gradient tiles
   int n_slices = 0;     // (max, sum exp) pairs per row
   int splits = 0;       // k-splits of the dH contraction
-  uint64_t p_off = 0, part_off = 0, scat_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0, total = 0;
+  uint64_t w_off = 0, p_off = 0, part_off = 0, scat_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0,
+           total = 0;
 };
 
 Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t esz) {
@@ -39,6 +40,8 @@ Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t
   L.splits = dh_splits(C, d, V);
   const int64_t tile_rows = (C + 63) / 64;
   uint64_t off = 0;
+  L.w_off = off;  // tiled copy of W
+  off += align256((uint64_t)((V + 63) / 64) * tile_row_stride(d) * esz);
   L.p_off = off;
   off += align256((uint64_t)tile_rows * L.pblk * esz);
   L.part_off = off;
@@ -206,6 +209,7 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
   st = get_workspace(dev, stream, L.total, &ws);
   if (st != CKL_OK) return st;
   char* base = (char*)ws;
+  void* Wt = base + L.w_off;
   void* P = base + L.p_off;
   float2* part = (float2*)(base + L.part_off);
   float* scat = (float*)(base + L.scat_off);
@@ -217,13 +221,14 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
   {
     Timed t(T_OTHER, stream);
     CKL_TRY(launch_mask_count(mask, N, scal, stream));
+    CKL_TRY(launch_tile_copy(dt, W, V, d, Wt, stream));
   }
   for (int64_t r0 = 0; r0 < N; r0 += L.C) {
     const int64_t rows = (N - r0) < L.C ? (N - r0) : L.C;
     const void* Hc = (const char*)H + (size_t)r0 * d * esz;
     {
       Timed t(T_LOGITS, stream);
-      CKL_TRY(launch_logits(dt, W, Hc, V, d, rows, P, L.pblk, part, L.n_slices, stream));
+      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, stream));
     }
     {
       RowArgs a{};
@@ -251,7 +256,7 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
     if (splits > cap) splits = (int)cap;
     {
       Timed t(T_DH, stream);
-      CKL_TRY(launch_dh(dt, P, L.pblk, W, V, d, rows, slab, splits, stream));
+      CKL_TRY(launch_dh(dt, P, L.pblk, Wt, V, d, rows, slab, splits, stream));
     }
     {
       Timed t(T_DHRED, stream);

@@ -429,6 +429,15 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int q = 0; q < NMF; ++q)
           acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+        if constexpr (!AK && !BKM) {
+          // both operands come through transpose reads (two per fragment):
+          // pin one MFMA, two LDS reads, ... (measured faster for this shape)
+#pragma unroll
+          for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        }
       } else {
 #pragma unroll
         for (int q = 0; q < NMF / 2; ++q)

@@ -42,10 +42,10 @@ int dh_splits(int64_t rows, int64_t d, int64_t V) {
   return best;
 }
 
-hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
+hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
                          int64_t pblk, float2* part, int n_slices, hipStream_t s) {
   GemmParams p{};
-  p.a = Operand{W, d, V, d, 0};
+  p.a = Operand{Wt, 0, V, d, tile_row_stride(d)};  // tiled: storage row = vocabulary id, column = d
   p.b = Operand{Hc, d, rows, d, 0};
   p.tiles_m = cdiv64(V, 256);
   p.tiles_n = cdiv64(rows, 256);
@@ -64,13 +64,13 @@ hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int
   return run<float, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
 }
 
-hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* W, int64_t V, int64_t d, int64_t rows,
+hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,
                      float* slab, int splits, hipStream_t s) {
   const int bn = d_tile(d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
   p.a = Operand{G, 0, rows, V, gblk};  // tiled: storage row = token, column = vocabulary id
-  p.b = Operand{W, d, d, V, 0};        // storage row = vocabulary id (k), column = d (n)
+  p.b = Operand{Wt, 0, d, V, tile_row_stride(d)};  // tiled: storage row = vocabulary id (k), column = d (n)
   p.tiles_m = cdiv64(rows, 256);
   p.tiles_n = cdiv64(d, bn);
   p.k_tiles = cdiv64(V, bk);
@@ -115,6 +115,31 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int6
   }
   if (bn == 192) return run<float, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
   return run<float, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
+}
+
+// ---------------------------------------------------------------- tiled copy
+template <typename T>
+__global__ void __launch_bounds__(256) tile_copy_kernel(const T* __restrict__ src, int64_t rows, int64_t cols,
+                                                       T* __restrict__ dst, int64_t dblk) {
+  constexpr int EPC = 16 / sizeof(T);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_row = cols / EPC;
+  if (i >= rows * per_row) return;
+  const int64_t r = i / per_row, c = (i - r * per_row) * EPC;
+  const u32x4 v = *(const u32x4*)(src + r * cols + c);
+  *(u32x4*)(dst + (r >> 6) * dblk + (c >> 6) * 4096 + (r & 63) * 64 + (c & 63)) = v;
+}
+
+hipError_t launch_tile_copy(Dtype dt, const void* src, int64_t rows, int64_t cols, void* dst, hipStream_t s) {
+  const int64_t n = rows * cols / (dt == DT_BF16 ? 8 : 4);
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(tile_copy_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, (const __bf16*)src, rows, cols,
+                       (__bf16*)dst, tile_row_stride(cols));
+  else
+    hipLaunchKernelGGL(tile_copy_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)src, rows, cols,
+                       (float*)dst, tile_row_stride(cols));
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- split-K reduce

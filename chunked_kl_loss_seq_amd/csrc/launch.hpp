@@ -11,16 +11,22 @@ enum Dtype : int { DT_BF16 = 0, DT_F32 = 1 };
 // Elements between two 64-row tile rows of a 64 x 64-tiled matrix with V columns.
 inline int64_t tile_row_stride(int64_t V) { return ((V + 63) / 64) * 4096; }
 
+// Copy of a row-major [rows, cols] matrix (cols % 8 == 0) into the 64 x 64
+// tiled layout, tile rows tile_row_stride(cols) elements apart.
+hipError_t launch_tile_copy(Dtype dt, const void* src, int64_t rows, int64_t cols, void* dst, hipStream_t s);
+
 // Logits of one chunk, kept as exp values: per (row n < rows, 128-id slice s)
 // the slice max m and sum of exp(z - m) into part[n][s], and exp(z - m) for
 // every z = H_c[n] . W[v] into P (element type of dt, tiled, tile rows pblk
 // elements apart).
-hipError_t launch_logits(Dtype dt, const void* W, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
+// W is the tiled copy of the weight (tile_row_stride(d) elements between tile rows).
+hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
                          int64_t pblk, float2* part, int n_slices, hipStream_t s);
 
 // dH partial slabs of one chunk: slab[s][n][j] = sum over the s-th vocabulary
-// split of G[n][v] W[v][j].  G is tiled like P, tile rows gblk elements apart.
-hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* W, int64_t V, int64_t d, int64_t rows,
+// split of G[n][v] W[v][j].  G is tiled like P, tile rows gblk elements apart;
+// Wt is the tiled copy of the weight.
+hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,
                      float* slab, int splits, hipStream_t s);
 // dH rows = sum of the slabs in split order, rounded once to the output type.
 hipError_t launch_dh_reduce(Dtype dt, const float* slab, int splits, int64_t rows, int64_t d, void* dH,

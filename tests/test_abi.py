@@ -40,7 +40,8 @@ def ws_formula(N, d, V, K, C, splits, esz=2):
     pblk = -(-V // 64) * 4096          # elements between 64-row tile rows of the exp / gradient tiles
     tile_rows = -(-C // 64)
     nsl = -(-V // 128)
-    return (a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
+    wt = -(-V // 64) * (-(-d // 64) * 4096)  # tiled copy of W
+    return (a(wt * esz) + a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
             + 2 * a(N * 4) + 256)
 
 
