@@ -55,6 +55,51 @@ def traffic_from_profile(kernel_kind):
         return None
 
 
+KERNEL_SYMBOLS = {  # GEMM kind -> the EPI template argument its kernel name carries
+    "logits": "ELb1ELb1ELi0E", "dh": "ELb1ELb0ELi1E", "dw": "ELb0ELb0ELi2E"}
+
+
+def _counter_per_launch(path, name_filter, counter):
+    import csv
+
+    vals = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and name_filter(r["Kernel_Name"]):
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows matched in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, commands):
+    """Write profiles/<kind>_gemm_hbm_traffic.json from rocprofv3 --pmc counter
+    files: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of each GEMM, each
+    scaled by what the same counter reads for a plain device copy of 1 GiB."""
+    is_copy = lambda n: "copyBuffer" in n  # noqa: E731
+    cal_f, _ = _counter_per_launch(cal_fetch_csv, is_copy, "FETCH_SIZE")
+    cal_w, _ = _counter_per_launch(cal_write_csv, is_copy, "WRITE_SIZE")
+    copy_kib = float(1 << 20)
+    sf, sw = copy_kib / cal_f, copy_kib / cal_w
+    sha = source_hash(GEMM_SOURCES)
+    for kind, tag in KERNEL_SYMBOLS.items():
+        sel = lambda n, tag=tag: "gemm_kernel" in n and tag in n  # noqa: E731
+        f, nf = _counter_per_launch(fetch_csv, sel, "FETCH_SIZE")
+        w, nw = _counter_per_launch(write_csv, sel, "WRITE_SIZE")
+        rec = {"kernel": f"{kind} GEMM", "source_sha": sha, "launches": [nf, nw],
+               "fetch_kib_per_launch_raw": f, "write_kib_per_launch_raw": w,
+               "copy_calibration": {"bytes": 1 << 30, "fetch_kib": cal_f, "write_kib": cal_w,
+                                    "fetch_scale": sf, "write_scale": sw},
+               "fetch_bytes_per_launch": f * sf * 1024, "write_bytes_per_launch": w * sw * 1024,
+               "bytes_per_launch": (f * sf + w * sw) * 1024, "commands": commands}
+        out = os.path.join(ROOT, "profiles", f"{kind}_gemm_hbm_traffic.json")
+        with open(out, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        log(f"[traffic] {kind}: fetch {rec['fetch_bytes_per_launch'] / 1e9:.2f} GB, "
+            f"write {rec['write_bytes_per_launch'] / 1e9:.2f} GB per launch -> {out}")
+
+
 def cpu_baseline(number, rows):
     """The oracle as it stands, timed on the host cores over a bounded sample."""
     import numpy as np  # noqa: F401
@@ -85,11 +130,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="named workload number (4 = gpt-oss head, 32K tokens)")
     ap.add_argument("--chunk", type=int, default=-1, help="rows per chunk (default: the workload's own)")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="positions in the oracle's timed sample")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="host only: turn rocprofv3 --pmc counter files into the per-GEMM traffic records")
+    ap.add_argument("--traffic-commands", default="", help="the profiling commands, stored with the records")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, commands=args.traffic_commands)
+        return
 
     if args.copy_calibration:
         import torch

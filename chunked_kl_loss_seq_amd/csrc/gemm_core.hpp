@@ -150,9 +150,10 @@ __device__ inline i32x4 make_rsrc(const void* base) {
 // pass, which cannot tell these LDS writes apart from the fragment reads of
 // other stages, does not put a full vmcnt wait in front of every LDS read;
 // the kernel orders them itself with explicit vmcnt waits and barriers.  The
-// instruction has no destination VGPRs.
+// instruction has no destination VGPRs.  On GFX9 an LDS DMA must not follow a
+// scalar write of M0 directly (one wait state), hence the s_nop.
 __device__ inline void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
                "s"(lds_addr)
                : "memory", "m0");
 }
