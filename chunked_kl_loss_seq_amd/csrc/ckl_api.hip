@@ -37,7 +37,7 @@ Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t
   L.C = C;
   L.pblk = tile_row_stride(V);
   L.n_slices = (int)((V + 127) / 128);
-  L.splits = dh_splits(C, d, V);
+  L.splits = dh_splits(esz == 2 ? DT_BF16 : DT_F32, C, d, V);
   const int64_t tile_rows = (C + 63) / 64;
   uint64_t off = 0;
   L.w_off = off;  // tiled copy of W
@@ -251,7 +251,7 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
       CKL_TRY(launch_dense(dt, a, stream));
       CKL_TRY(launch_scatter(dt, a, stream));
     }
-    int splits = dh_splits(rows, d, V);
+    int splits = dh_splits(dt, rows, d, V);
     const int64_t cap = (int64_t)L.splits * L.C / rows;  // slab capacity in splits of this chunk
     if (splits > cap) splits = (int)cap;
     {

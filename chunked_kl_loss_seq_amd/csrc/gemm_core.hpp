@@ -144,6 +144,13 @@ __device__ inline i32x4 make_rsrc(const void* base) {
   return r;
 }
 
+// A 64-bit value the caller knows to be wave-uniform, kept in SGPRs.
+__device__ inline uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // buffer_load_dwordx4 ... lds: lane l's 16 bytes at byte `voff` of the
 // resource go to LDS byte lds_addr + 16 l (lds_addr is wave-uniform and goes
 // through M0).  Written as inline assembly so that the compiler's wait-count
@@ -224,20 +231,35 @@ struct SlabDMA {
     }
   }
 
-  // Issue the copy of slab origin k0 into `lds` (a wave-uniform LDS address);
-  // `spare` is 1 KiB of LDS that padding loads may overwrite.
-  __device__ inline void issue(const Operand& o, int64_t mn0, int64_t k0, char* lds, int wave, char* spare) const {
-    const T* base = (const T*)o.ptr + (KMAJ ? elem_offset(o, mn0, k0) : elem_offset(o, k0, mn0));
-    const i32x4 rs = make_rsrc(base);
-    const bool tail = k0 + kBK > o.k_ext;
-    const int kleft = tail ? (int)(o.k_ext - k0) : kBK;  // <= 0 when the slab is past the end
+  // Element offset of the slab at depth k0 from the slab at depth 0 (same
+  // tile origin).  It depends on k0 and the layout only, so a tile keeps one
+  // base address and advances it per slab with scalar arithmetic.
+  __device__ static inline int64_t slab_off(const Operand& o, int64_t k0) {
+    if (KMAJ) return o.blk ? (k0 >> 6) * 4096 + (k0 & 63) : k0;
+    return o.blk ? (k0 >> 6) * o.blk + (k0 & 63) * 64 : k0 * o.ld;
+  }
+
+  // Issue the copy of a whole slab (every k inside the operand) whose origin
+  // is at byte address `base` into this wave's blocks of the stage at LDS byte
+  // address `lds` (wave-uniform; blocks of other waves are 1 KiB apart).
+  __device__ inline void issue_full(uint64_t base, uint32_t lds, int wave, uint32_t spare) const {
+    const i32x4 rs = make_rsrc((const void*)base);
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const bool real = has(wave, i);
-      uint32_t v = voff[i];
-      if (!real || (tail && (int)kd[i] >= kleft)) v = kOOB;
-      char* dst = real ? lds + (i * NW + wave) * 1024 : spare;
-      dma16(rs, v, lds_addr(dst));
+      dma16(rs, real ? voff[i] : kOOB, real ? lds + (uint32_t)((i * NW + wave) * 1024) : spare);
+    }
+  }
+
+  // Same for a slab that reaches past k_ext: only the first kleft k (none when
+  // kleft <= 0) are loaded, the rest read as zeros without touching memory.
+  __device__ inline void issue_tail(uint64_t base, uint32_t lds, int wave, uint32_t spare, int kleft) const {
+    const i32x4 rs = make_rsrc((const void*)base);
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+      const bool real = has(wave, i);
+      const uint32_t v = (!real || (int)kd[i] >= kleft) ? kOOB : voff[i];
+      dma16(rs, v, real ? lds + (uint32_t)((i * NW + wave) * 1024) : spare);
     }
   }
 };
@@ -366,7 +388,8 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   constexpr int STAGE = DA::kBytes + DB::kBytes;
   constexpr int SPARE = DA::kSpare > DB::kSpare ? DA::kSpare : DB::kSpare;
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + SPARE];
-  char* spare = smem + NS * STAGE;
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t spare = lds0 + NS * STAGE;
 
   const TileCoord tc = tile_coord(p);
   if (!tc.valid) return;
@@ -391,20 +414,41 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   DB db;
   da.init(p.a, m0, wave, lane);
   db.init(p.b, n0, wave, lane);
+  // byte addresses of the tile's slab origins at k = 0 (wave-uniform)
+  const uint64_t a_org = uniform64((uint64_t)p.a.ptr + sizeof(T) * (uint64_t)(AK ? elem_offset(p.a, m0, 0)
+                                                                               : elem_offset(p.a, 0, m0)));
+  const uint64_t b_org = uniform64((uint64_t)p.b.ptr + sizeof(T) * (uint64_t)(BKM ? elem_offset(p.b, n0, 0)
+                                                                                : elem_offset(p.b, 0, n0)));
+
+  // Copy slab kt into stage st.  A slab past the tile's k range is skipped
+  // when skip is set (the waits then count fewer loads, which only the
+  // two-stage ring, whose waits drain everything, tolerates), otherwise it
+  // is issued as out-of-range loads so every wave keeps NIT loads per slab.
+  auto issue = [&](int kt, int st, bool skip) {
+    const int64_t k0 = (int64_t)kt * BK;
+    const uint32_t sa_lds = lds0 + (uint32_t)(st * STAGE), sb_lds = sa_lds + DA::kBytes;
+    if (kt < kt_end && k0 + BK <= p.a.k_ext) {
+      da.issue_full(a_org + sizeof(T) * (uint64_t)DA::slab_off(p.a, k0), sa_lds, wave, spare);
+      db.issue_full(b_org + sizeof(T) * (uint64_t)DB::slab_off(p.b, k0), sb_lds, wave, spare);
+    } else if (kt < kt_end || !skip) {
+      const int kleft = kt < kt_end ? (int)(p.a.k_ext - k0) : 0;
+      da.issue_tail(kt < kt_end ? a_org + sizeof(T) * (uint64_t)DA::slab_off(p.a, k0) : a_org, sa_lds, wave, spare,
+                    kleft);
+      db.issue_tail(kt < kt_end ? b_org + sizeof(T) * (uint64_t)DB::slab_off(p.b, k0) : b_org, sb_lds, wave, spare,
+                    kleft);
+    }
+  };
 
   // Ring of NS LDS stages.  At the top of iteration kt the stage cur holds
   // slab kt and the other stages hold (or are loading) slabs kt+1 .. kt+NS-1.
   // In the last sub-step of iteration kt each wave waits for its part of slab
   // kt+1, the workgroup synchronises half-way through the MFMAs, the first
   // fragments of slab kt+1 load, slab kt+NS is issued into stage cur (no wave
-  // reads it any more), and the second half of the MFMAs runs.  Slabs past the
-  // end read out-of-range offsets or unused data and are never consumed, so
-  // the loop body has no data-dependent branches.
+  // reads it any more), and the second half of the MFMAs runs.  The loop is
+  // unrolled over the NS stages so that every LDS address is a constant offset
+  // from a per-lane base.
 #pragma unroll
-  for (int st = 0; st < NS; ++st) {
-    da.issue(p.a, m0, (int64_t)(kt_begin + st) * BK, smem + st * STAGE, wave, spare);
-    db.issue(p.b, n0, (int64_t)(kt_begin + st) * BK, smem + st * STAGE + DA::kBytes, wave, spare);
-  }
+  for (int st = 0; st < NS; ++st) issue(kt_begin + st, st, false);
   wait_vmcnt<(NS - 1) * NIT>();
   __syncthreads();
 #pragma unroll
@@ -412,52 +456,57 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
   for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(smem + DA::kBytes, wn * WTN + j * 32, 0, lane);
 
-  int cur = 0;
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int nxt = cur + 1 == NS ? 0 : cur + 1;
-    char* sa = smem + cur * STAGE;
-    char* sb = sa + DA::kBytes;
-    char* na = smem + nxt * STAGE;
-    char* nb = na + DA::kBytes;
+  for (int kt0 = kt_begin; kt0 < kt_end; kt0 += NS) {
 #pragma unroll
-    for (int kk = 0; kk < SUB; ++kk) {
-      const int fbuf = kk & 1;
-      if (kk + 1 < SUB) {
+    for (int cur = 0; cur < NS; ++cur) {
+      const int kt = kt0 + cur;
+      if (kt >= kt_end) break;
+      const int nxt = cur + 1 == NS ? 0 : cur + 1;
+      const char* sa = smem + cur * STAGE;
+      const char* sb = sa + DA::kBytes;
+      const char* na = smem + nxt * STAGE;
+      const char* nb = na + DA::kBytes;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[fbuf ^ 1][i] = load_frag<T, BM, AK, KB>(sa, wm * WTM + i * 32, kk + 1, lane);
+      for (int kk = 0; kk < SUB; ++kk) {
+        const int fbuf = kk & 1;
+        if (kk + 1 < SUB) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fb[fbuf ^ 1][j] = load_frag<T, BN, BKM, KB>(sb, wn * WTN + j * 32, kk + 1, lane);
+          for (int i = 0; i < FM; ++i)
+            fa[fbuf ^ 1][i] = load_frag<T, BM, AK, KB>(sa, wm * WTM + i * 32, kk + 1, lane);
 #pragma unroll
-        for (int q = 0; q < NMF; ++q)
-          acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
-        if constexpr (!AK && !BKM) {
-          // both operands come through transpose reads (two per fragment):
-          // pin one MFMA, two LDS reads, ... (measured faster for this shape)
+          for (int j = 0; j < FN; ++j)
+            fb[fbuf ^ 1][j] = load_frag<T, BN, BKM, KB>(sb, wn * WTN + j * 32, kk + 1, lane);
 #pragma unroll
-          for (int q = 0; q < NMF; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          for (int q = 0; q < NMF; ++q)
+            acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+          if constexpr (!AK && !BKM) {
+            // both operands come through transpose reads (two per fragment):
+            // pin one MFMA, two LDS reads, ... (measured faster for this shape)
+#pragma unroll
+            for (int q = 0; q < NMF; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
           }
+        } else {
+#pragma unroll
+          for (int q = 0; q < NMF / 2; ++q)
+            acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+          wait_vmcnt<(NS - 2) * NIT>();
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < FM; ++i) fa[0][i] = load_frag<T, BM, AK, KB>(na, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(nb, wn * WTN + j * 32, 0, lane);
+          issue(kt + NS, cur, NS == 2);
+#pragma unroll
+          for (int q = NMF / 2; q < NMF; ++q)
+            acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
         }
-      } else {
-#pragma unroll
-        for (int q = 0; q < NMF / 2; ++q)
-          acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
-        wait_vmcnt<(NS - 2) * NIT>();
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[0][i] = load_frag<T, BM, AK, KB>(na, wm * WTM + i * 32, 0, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(nb, wn * WTN + j * 32, 0, lane);
-        da.issue(p.a, m0, (int64_t)(kt + NS) * BK, sa, wave, spare);
-        db.issue(p.b, n0, (int64_t)(kt + NS) * BK, sb, wave, spare);
-#pragma unroll
-        for (int q = NMF / 2; q < NMF; ++q)
-          acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
       }
     }
-    cur = nxt;
   }
+  wait_vmcnt<0>();  // no LDS copy outlives the workgroup
 
   // ------------------------------------------------------------ epilogues
   // Lane l, accumulator slot r of block (i, j) holds D[row][col] with

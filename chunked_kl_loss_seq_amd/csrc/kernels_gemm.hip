@@ -21,12 +21,18 @@ hipError_t run(GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
-int d_tile(int64_t d) { return (d % 192 == 0 && d % 256 != 0) ? 192 : 256; }
+// bf16: 256-wide tiles along d (8 waves of 128 x 64), measured faster than
+// 192-wide ones even where 192 divides d and 256 does not; fp32 (wider
+// fragments, register-bound): 192 where it divides d.
+int d_tile(Dtype dt, int64_t d) {
+  if (dt == DT_BF16) return 256;
+  return (d % 192 == 0 && d % 256 != 0) ? 192 : 256;
+}
 
-int dh_splits(int64_t rows, int64_t d, int64_t V) {
+int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
   // Pick the k-split count (1..8) that best fills whole waves of 256
   // workgroups; each split keeps at least 16 k-steps.
-  const int tiles = cdiv64(rows, 256) * cdiv64(d, d_tile(d));
+  const int tiles = cdiv64(rows, 256) * cdiv64(d, d_tile(dt, d));
   const int ksteps = cdiv64(V, 64);
   int best = 1;
   double best_eff = -1.0;
@@ -66,7 +72,7 @@ hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, in
 
 hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,
                      float* slab, int splits, hipStream_t s) {
-  const int bn = d_tile(d);
+  const int bn = d_tile(dt, d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
   p.a = Operand{G, 0, rows, V, gblk};  // tiled: storage row = token, column = vocabulary id
@@ -83,17 +89,14 @@ hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int6
   p.valid_m = rows;
   p.valid_n = d;
   if (p.splits != splits) return hipErrorInvalidValue;
-  if (dt == DT_BF16) {
-    if (bn == 192) return run<__bf16, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
-    return run<__bf16, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
-  }
+  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, true, false, EPI_SLAB, 128, 2>(p, s);
   if (bn == 192) return run<float, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
   return run<float, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
 }
 
 hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int64_t V, int64_t d, int64_t rows,
                      float* dW, int beta, hipStream_t s) {
-  const int bn = d_tile(d);
+  const int bn = d_tile(dt, d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
   p.a = Operand{G, 0, V, rows, gblk};  // tiled: storage row = token (k), column = vocabulary id (m)
@@ -109,10 +112,7 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int6
   p.valid_m = V;
   p.valid_n = d;
   p.beta = beta;
-  if (dt == DT_BF16) {
-    if (bn == 192) return run<__bf16, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
-    return run<__bf16, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
-  }
+  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, false, false, EPI_ACCUM, 128, 2>(p, s);
   if (bn == 192) return run<float, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
   return run<float, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
 }

@@ -36,9 +36,9 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int6
                      float* dW, int beta, hipStream_t s);
 
 // k-splits used for the dH contraction of a chunk of `rows` rows.
-int dh_splits(int64_t rows, int64_t d, int64_t V);
+int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V);
 // tile width used along d by the dH and dW contractions.
-int d_tile(int64_t d);
+int d_tile(Dtype dt, int64_t d);
 
 // Valid-token count n and scale 1/n (0 if n = 0) into scal (int64 n, float s).
 hipError_t launch_mask_count(const uint8_t* mask, int64_t N, void* scal, hipStream_t s);
