@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="named workload number (4 = gpt-oss head, 32K tokens)")
     ap.add_argument("--chunk", type=int, default=-1, help="rows per chunk (default: the workload's own)")
+    ap.add_argument("--variant", choices=["fused", "two-pass"], default="fused",
+                    help="fused: one ckl_fwd_bwd call per step; two-pass: ckl_fwd then ckl_bwd (logits recomputed)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -189,9 +191,24 @@ def main():
     dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     del inp["H"], inp["W"]
 
+    two_pass = args.variant == "two-pass"
+    row_lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    if two_pass:
+        C1, ws1 = binding.plan(N, d, V, K, wl.dtype, chunk, pass_="fwd")
+        C, ws_plan = binding.plan(N, d, V, K, wl.dtype, chunk, pass_="bwd")
+        ws_plan = max(ws_plan, ws1)
+        log(f"[bench] two-pass: forward chunk {C1} rows, backward chunk {C} rows")
+
+    def step():
+        if two_pass:
+            binding.fwd(H, W, ids, T, mask, chunk, out_loss=loss, row_lse=row_lse)
+            binding.bwd(H, W, ids, T, row_lse, mask, chunk=chunk, dH=dH, dW=dW)
+        else:
+            binding.fwd_bwd(H, W, ids, T, mask, chunk, out_loss=loss, dH=dH, dW=dW)
+
     log(f"[bench] chunk {C} rows, planned workspace {ws_plan / 2**30:.3f} GiB; warmup {args.warmup}")
     for _ in range(args.warmup):
-        binding.fwd_bwd(H, W, ids, T, mask, chunk, out_loss=loss, dH=dH, dW=dW)
+        step()
     torch.cuda.synchronize()
     log(f"[bench] warm, loss {loss.item():.6f}; timing {args.steps} steps")
 
@@ -202,7 +219,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        binding.fwd_bwd(H, W, ids, T, mask, chunk, out_loss=loss, dH=dH, dW=dW)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
@@ -213,17 +230,19 @@ def main():
     binding.timing_enable(False)
     ws_held = binding.workspace_bytes_held()
 
-    flop_gemm_launch_total = 2.0 * n_valid * d * V * args.steps  # per GEMM kind over the timed region
+    flop_gemm_launch_total = 2.0 * n_valid * d * V * args.steps  # per GEMM kind (and pass) over the timed region
+    logits_passes = 2 if two_pass else 1  # the two-pass backward recomputes the logits
     gemm = {k: kinds[k] for k in ("logits", "dh", "dw")}
-    dom = max(gemm, key=lambda k: gemm[k][0])
+    dom = max(gemm, key=lambda k: gemm[k][0] / (logits_passes if k == "logits" else 1))
     dom_ms, dom_n = gemm[dom]
-    achieved = flop_gemm_launch_total / (dom_ms / 1e3) / 1e12
-    total_tflops = 6.0 * n_valid * d * V / (ms / 1e3) / 1e12
+    achieved = flop_gemm_launch_total * (logits_passes if dom == "logits" else 1) / (dom_ms / 1e3) / 1e12
+    total_tflops = (6.0 + 2.0 * (logits_passes - 1)) * n_valid * d * V / (ms / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
     per_kernel = {k: {"ms_per_step": kinds[k][0] / args.steps, "launches_per_step": kinds[k][1] / args.steps}
                   for k in kinds}
     for k in ("logits", "dh", "dw"):
-        per_kernel[k]["tflops"] = flop_gemm_launch_total / (kinds[k][0] / 1e3) / 1e12 if kinds[k][0] else None
+        f = flop_gemm_launch_total * (logits_passes if k == "logits" else 1)
+        per_kernel[k]["tflops"] = f / (kinds[k][0] / 1e3) / 1e12 if kinds[k][0] else None
     traffic = traffic_from_profile(dom)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": f"{dom} GEMM",
@@ -239,8 +258,11 @@ def main():
         cpu = cpu_baseline(args.workload, args.cpu_rows)
         log(f"[bench] oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
+    metric = "fused KL fwd+bwd tokens/s + MFMA TFLOP/s % peak; peak workspace GiB"
+    if two_pass:
+        metric = "chunked KL forward + recomputing backward (two calls) tokens/s; MFMA TFLOP/s % peak; workspace GiB"
     out = {
-        "metric": "fused KL fwd+bwd tokens/s + MFMA TFLOP/s % peak; peak workspace GiB",
+        "metric": metric,
         "value": round(N / (ms / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -252,7 +274,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "N": N, "valid_tokens": n_valid, "d": d, "V": V, "K": K, "chunk": C,
+        "config": {"workload": wl.name, "variant": args.variant, "N": N, "valid_tokens": n_valid, "d": d, "V": V,
+                   "K": K, "chunk": C,
                    "global_batch": N // (wl.seq_len or N), "seq_len": wl.seq_len or N, "parallelism": "none"},
         "tokens_per_s_valid": round(n_valid / (ms / 1e3), 1),
         "tflops": round(total_tflops, 2),

@@ -5,10 +5,13 @@
 """
 from .binding import (  # noqa: F401
     CklError,
+    bwd,
     debug_rows,
     fused_kl,
+    fwd,
     fwd_bwd,
     plan,
+    recompute_kl,
     release_workspace,
     timing_enable,
     timing_query,

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libckl.so")
 CKL_OK = 0
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
+PASSES = {"fused": 0, "fwd": 1, "bwd": 2}
 TIMING_KINDS = {"logits": 0, "rows": 1, "dh": 2, "dh_reduce": 3, "dw": 4, "other": 5}
 
 _lib = None
@@ -43,6 +44,12 @@ def lib():
     L.ckl_fwd_bwd_ex.restype = ctypes.c_int
     L.ckl_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, i64, u64, ctypes.POINTER(i64), ctypes.POINTER(u64)]
     L.ckl_plan.restype = ctypes.c_int
+    L.ckl_plan_pass.argtypes = [ctypes.c_int] + L.ckl_plan.argtypes
+    L.ckl_plan_pass.restype = ctypes.c_int
+    L.ckl_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp]
+    L.ckl_fwd.restype = ctypes.c_int
+    L.ckl_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]
+    L.ckl_bwd.restype = ctypes.c_int
     L.ckl_release_workspace.argtypes = []
     L.ckl_release_workspace.restype = None
     L.ckl_workspace_bytes_held.argtypes = []
@@ -68,12 +75,14 @@ def _check(st, what):
         raise CklError(st, what)
 
 
-def plan(N, d, V, K, dtype="bf16", chunk=0, budget_bytes=0):
-    """(chunk rows, workspace bytes) the library will use for this shape."""
+def plan(N, d, V, K, dtype="bf16", chunk=0, budget_bytes=0, pass_="fused"):
+    """(chunk rows, workspace bytes) the library will use for this shape and call
+    (``pass_`` = "fused", "fwd" or "bwd")."""
     c = ctypes.c_int64(0)
     b = ctypes.c_uint64(0)
     dt = DTYPE_BF16 if dtype == "bf16" else DTYPE_F32
-    _check(lib().ckl_plan(N, d, V, K, dt, chunk, budget_bytes, ctypes.byref(c), ctypes.byref(b)), "ckl_plan")
+    _check(lib().ckl_plan_pass(PASSES[pass_], N, d, V, K, dt, chunk, budget_bytes, ctypes.byref(c),
+                               ctypes.byref(b)), "ckl_plan_pass")
     return int(c.value), int(b.value)
 
 
@@ -140,6 +149,60 @@ def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=No
     return out_loss, dH, dW
 
 
+def _check_inputs(torch, H, W, ids, tlogit, what):
+    if not H.is_cuda:
+        raise ValueError(f"{what} needs GPU tensors")
+    for name, t in (("H", H), ("W", W), ("ids", ids), ("tlogit", tlogit)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if ids.dtype != torch.int32 or tlogit.dtype != torch.float32:
+        raise ValueError("ids must be int32 and tlogit float32")
+    if H.dtype != W.dtype or H.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("H and W must both be bfloat16 or both float32")
+    return DTYPE_BF16 if H.dtype == torch.bfloat16 else DTYPE_F32
+
+
+def fwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, row_lse=None, row_kl=None):
+    """Forward only: (loss 0-dim float32, row_lse float32 [N]); row_kl [N] filled when given."""
+    import torch
+
+    dt = _check_inputs(torch, H, W, ids, tlogit, "fwd")
+    N, d = H.shape
+    V, K = W.shape[0], ids.shape[1]
+    if mask is not None:
+        mask = mask.to(torch.uint8).contiguous()
+    if out_loss is None:
+        out_loss = torch.empty((), dtype=torch.float32, device=H.device)
+    if row_lse is None:
+        row_lse = torch.empty((N,), dtype=torch.float32, device=H.device)
+    st = lib().ckl_fwd(dt, _ptr(H), _ptr(W), _ptr(ids), _ptr(tlogit), _ptr(mask), N, d, V, K, int(chunk),
+                       _ptr(out_loss), _ptr(row_lse), _ptr(row_kl), _stream(torch, H.device))
+    _check(st, "ckl_fwd")
+    return out_loss, row_lse
+
+
+def bwd(H, W, ids, tlogit, row_lse, mask=None, grad_loss=None, chunk=0, dH=None, dW=None):
+    """Backward that recomputes the logits: (dH like H, dW float32 [V,d]) of
+    grad_loss x loss; grad_loss is a float32 device scalar tensor or None (1)."""
+    import torch
+
+    dt = _check_inputs(torch, H, W, ids, tlogit, "bwd")
+    N, d = H.shape
+    V, K = W.shape[0], ids.shape[1]
+    if mask is not None:
+        mask = mask.to(torch.uint8).contiguous()
+    if grad_loss is not None:
+        grad_loss = grad_loss.to(device=H.device, dtype=torch.float32).contiguous()
+    if dH is None:
+        dH = torch.empty_like(H)
+    if dW is None:
+        dW = torch.empty((V, d), dtype=torch.float32, device=H.device)
+    st = lib().ckl_bwd(dt, _ptr(H), _ptr(W), _ptr(ids), _ptr(tlogit), _ptr(mask), _ptr(row_lse),
+                       _ptr(grad_loss), N, d, V, K, int(chunk), _ptr(dH), _ptr(dW), _stream(torch, H.device))
+    _check(st, "ckl_bwd")
+    return dH, dW
+
+
 def debug_rows(Z, ids, tlogit, mask=None, scale=1.0, g_bf16=True):
     """Row pass alone on caller-given fp32 logits Z [R,V] (synchronises)."""
     import torch
@@ -203,3 +266,40 @@ class _FusedKL:
 def fused_kl(H, W, ids, tlogit, mask=None, chunk=0):
     """Loss as a differentiable torch scalar: gradients were computed in the forward pass."""
     return _FusedKL.get().apply(H, W, ids, tlogit, mask, chunk)
+
+
+class _RecomputeKL:
+    """Two-pass autograd wrapper: the forward keeps the per-position log-normaliser,
+    the backward recomputes the logits (ckl_fwd / ckl_bwd)."""
+
+    _fn = None
+
+    @classmethod
+    def get(cls):
+        if cls._fn is None:
+            import torch
+
+            class RecomputeKL(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, H, W, ids, tlogit, mask, chunk):
+                    H, W = H.contiguous(), W.contiguous()
+                    loss, lse = fwd(H, W, ids, tlogit, mask, chunk)
+                    ctx.save_for_backward(H, W, ids, tlogit, lse, mask if mask is not None else torch.empty(0))
+                    ctx.has_mask = mask is not None
+                    ctx.chunk = chunk
+                    return loss
+
+                @staticmethod
+                def backward(ctx, g):
+                    H, W, ids, tlogit, lse, mask = ctx.saved_tensors
+                    dH, dW = bwd(H, W, ids, tlogit, lse, mask if ctx.has_mask else None,
+                                 grad_loss=g.reshape(()), chunk=ctx.chunk)
+                    return dH, dW.to(W.dtype), None, None, None, None
+
+            cls._fn = RecomputeKL
+        return cls._fn
+
+
+def recompute_kl(H, W, ids, tlogit, mask=None, chunk=0):
+    """Loss as a differentiable torch scalar whose backward recomputes each chunk's logits."""
+    return _RecomputeKL.get().apply(H, W, ids, tlogit, mask, chunk)

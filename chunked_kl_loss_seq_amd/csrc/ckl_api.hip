@@ -1,5 +1,6 @@
 // C ABI of the fused chunked KL loss: argument checks, chunk planner,
-// workspace cache and the chunk loop that enqueues the kernels.
+// workspace cache and the chunk loop that enqueues the kernels, for the fused
+// call and for the forward / recomputing-backward pair.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -22,6 +23,10 @@ constexpr int64_t kRowStep = 256;
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 inline int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Which call a chunk loop serves: the fused forward + backward, the forward
+// alone (loss and log-normalisers), or the backward that recomputes the logits.
+enum Pass : int { PASS_FUSED = CKL_PASS_FUSED, PASS_FWD = CKL_PASS_FWD, PASS_BWD = CKL_PASS_BWD };
+
 // Device workspace of one call with chunks of C rows.
 struct Layout {
   int64_t C = 0;
@@ -32,12 +37,12 @@ struct Layout {
            total = 0;
 };
 
-Layout make_layout(int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t esz) {
+Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t esz) {
   Layout L;
   L.C = C;
   L.pblk = tile_row_stride(V);
   L.n_slices = (int)((V + 127) / 128);
-  L.splits = dh_splits(esz == 2 ? DT_BF16 : DT_F32, C, d, V);
+  L.splits = pass == PASS_FWD ? 0 : dh_splits(esz == 2 ? DT_BF16 : DT_F32, C, d, V);
   const int64_t tile_rows = (C + 63) / 64;
   uint64_t off = 0;
   L.w_off = off;  // tiled copy of W
@@ -71,7 +76,8 @@ uint64_t budget_from_env(uint64_t b) {
   return kDefaultBudget;
 }
 
-int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_t budget, size_t esz, Layout* out) {
+int plan_impl(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_t budget, size_t esz,
+              Layout* out) {
   if (N <= 0 || d <= 0 || V <= 0 || K <= 0 || chunk < 0) return CKL_EINVAL;
   if (K > V) return CKL_EINVAL;
   if (d % 8 != 0 || K > kMaxK) return CKL_EUNSUPPORTED;
@@ -79,7 +85,7 @@ int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_
   budget = budget_from_env(budget);
   if (chunk > 0) {
     const int64_t C = chunk < N ? chunk : N;
-    Layout L = make_layout(N, d, V, K, C, esz);
+    Layout L = make_layout(pass, N, d, V, K, C, esz);
     if (L.total > budget) return CKL_EBUDGET;
     *out = L;
     return CKL_OK;
@@ -87,13 +93,13 @@ int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_
   // largest fitting multiple of 256 rows (or N itself when smaller)
   int64_t cmax = 0;
   if (N <= kRowStep) {
-    if (make_layout(N, d, V, K, N, esz).total <= budget) cmax = N;
+    if (make_layout(pass, N, d, V, K, N, esz).total <= budget) cmax = N;
   } else {
     int64_t lo = 1, hi = roundup(N, kRowStep) / kRowStep;  // in units of 256 rows
-    if (make_layout(N, d, V, K, kRowStep, esz).total > budget) return CKL_EBUDGET;
+    if (make_layout(pass, N, d, V, K, kRowStep, esz).total > budget) return CKL_EBUDGET;
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) / 2;
-      if (make_layout(N, d, V, K, mid * kRowStep, esz).total <= budget)
+      if (make_layout(pass, N, d, V, K, mid * kRowStep, esz).total <= budget)
         lo = mid;
       else
         hi = mid - 1;
@@ -107,7 +113,7 @@ int plan_impl(int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_
   int64_t C = roundup((N + nch - 1) / nch, kRowStep);
   if (C > cmax) C = cmax;
   if (C > N) C = N;
-  *out = make_layout(N, d, V, K, C, esz);
+  *out = make_layout(pass, N, d, V, K, C, esz);
   return CKL_OK;
 }
 
@@ -190,16 +196,26 @@ struct Timed {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, const float* tlogit,
-                 const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
-                 void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream) {
-  if (!H || !W || !ids || !tlogit || !out_loss || !dH || !dW) return CKL_EINVAL;
+// One call of any pass.  Inputs common to all: H, W, ids, tlogit, mask.
+//   PASS_FUSED: out_loss, dH, dW (+ optional row_kl, row_lse)
+//   PASS_FWD:   out_loss, row_lse (+ optional row_kl)
+//   PASS_BWD:   lse_in (the forward's row_lse), optional gscale; dH, dW
+int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* ids, const float* tlogit,
+             const uint8_t* mask, const float* lse_in, const float* gscale, int64_t N, int64_t d, int64_t V,
+             int64_t K, int64_t chunk, float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse,
+             hipStream_t stream) {
+  const bool want_loss = pass != PASS_BWD, want_grad = pass != PASS_FWD;
+  if (!H || !W || !ids || !tlogit) return CKL_EINVAL;
+  if (want_loss && !out_loss) return CKL_EINVAL;
+  if (want_grad && (!dH || !dW)) return CKL_EINVAL;
+  if (pass == PASS_FWD && !row_lse) return CKL_EINVAL;
+  if (pass == PASS_BWD && !lse_in) return CKL_EINVAL;
   if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return CKL_EINVAL;
   if (!aligned(ids, 4) || !aligned(tlogit, 4) || !aligned(out_loss, 4)) return CKL_EINVAL;
-  if (!aligned(row_kl, 4) || !aligned(row_lse, 4)) return CKL_EINVAL;
+  if (!aligned(row_kl, 4) || !aligned(row_lse, 4) || !aligned(lse_in, 4) || !aligned(gscale, 4)) return CKL_EINVAL;
   const size_t esz = dt == DT_BF16 ? 2 : 4;
   Layout L;
-  int st = plan_impl(N, d, V, K, chunk, 0, esz, &L);
+  int st = plan_impl(pass, N, d, V, K, chunk, 0, esz, &L);
   if (st != CKL_OK) return st;
   if ((N + L.C - 1) / L.C > (int64_t)1 << 24) return CKL_EUNSUPPORTED;
 
@@ -245,12 +261,17 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
       a.rows = rows;
       a.scat = scat;
       a.kl_out = kl + r0;
-      a.lse_out = lse + r0;
+      a.lse_out = pass == PASS_BWD ? nullptr : lse + r0;
+      a.lse_in = pass == PASS_BWD ? lse_in + r0 : nullptr;
+      a.gscale = pass == PASS_BWD ? gscale : nullptr;
       Timed t(T_ROWS, stream);
       CKL_TRY(launch_row_stats(dt, a, stream));
-      CKL_TRY(launch_dense(dt, a, stream));
-      CKL_TRY(launch_scatter(dt, a, stream));
+      if (want_grad) {
+        CKL_TRY(launch_dense(dt, a, stream));
+        CKL_TRY(launch_scatter(dt, a, stream));
+      }
     }
+    if (!want_grad) continue;
     int splits = dh_splits(dt, rows, d, V);
     const int64_t cap = (int64_t)L.splits * L.C / rows;  // slab capacity in splits of this chunk
     if (splits > cap) splits = (int)cap;
@@ -267,12 +288,15 @@ int fwd_bwd_impl(Dtype dt, const void* H, const void* W, const int32_t* ids, con
       CKL_TRY(launch_dw(dt, P, L.pblk, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, stream));
     }
   }
-  {
+  if (want_loss) {
     Timed t(T_OTHER, stream);
     CKL_TRY(launch_finalize(kl, N, scal, out_loss, stream));
   }
   return CKL_OK;
 }
+
+inline bool dtype_ok(int dtype) { return dtype == CKL_DTYPE_BF16 || dtype == CKL_DTYPE_F32; }
+inline Dtype to_dt(int dtype) { return dtype == CKL_DTYPE_BF16 ? DT_BF16 : DT_F32; }
 
 }  // namespace
 
@@ -282,8 +306,8 @@ int ckl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx, const flo
                 const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
                 void* dH, float* dW, hipStream_t stream) {
   try {
-    return fwd_bwd_impl(DT_BF16, H, W, topk_idx, topk_logit, mask, N, d, V, K, chunk, out_loss, dH, dW, nullptr,
-                        nullptr, stream);
+    return run_impl(PASS_FUSED, DT_BF16, H, W, topk_idx, topk_logit, mask, nullptr, nullptr, N, d, V, K, chunk,
+                    out_loss, dH, dW, nullptr, nullptr, stream);
   } catch (...) {
     return CKL_EHIP;
   }
@@ -293,8 +317,8 @@ int ckl_fwd_bwd_f32(const float* H, const float* W, const int32_t* topk_idx, con
                     const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
                     float* out_loss, float* dH, float* dW, hipStream_t stream) {
   try {
-    return fwd_bwd_impl(DT_F32, H, W, topk_idx, topk_logit, mask, N, d, V, K, chunk, out_loss, dH, dW, nullptr,
-                        nullptr, stream);
+    return run_impl(PASS_FUSED, DT_F32, H, W, topk_idx, topk_logit, mask, nullptr, nullptr, N, d, V, K, chunk,
+                    out_loss, dH, dW, nullptr, nullptr, stream);
   } catch (...) {
     return CKL_EHIP;
   }
@@ -303,21 +327,46 @@ int ckl_fwd_bwd_f32(const float* H, const float* W, const int32_t* topk_idx, con
 int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
                    const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
                    void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream) {
-  if (dtype != CKL_DTYPE_BF16 && dtype != CKL_DTYPE_F32) return CKL_EINVAL;
+  if (!dtype_ok(dtype)) return CKL_EINVAL;
   try {
-    return fwd_bwd_impl(dtype == CKL_DTYPE_BF16 ? DT_BF16 : DT_F32, H, W, topk_idx, topk_logit, mask, N, d, V, K,
-                        chunk, out_loss, dH, dW, row_kl, row_lse, stream);
+    return run_impl(PASS_FUSED, to_dt(dtype), H, W, topk_idx, topk_logit, mask, nullptr, nullptr, N, d, V, K, chunk,
+                    out_loss, dH, dW, row_kl, row_lse, stream);
   } catch (...) {
     return CKL_EHIP;
   }
 }
 
-int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
-             int64_t* chunk_out, uint64_t* workspace_bytes_out) {
-  if (dtype != CKL_DTYPE_BF16 && dtype != CKL_DTYPE_F32) return CKL_EINVAL;
+int ckl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+            const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
+            float* row_lse, float* row_kl, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return CKL_EINVAL;
+  try {
+    return run_impl(PASS_FWD, to_dt(dtype), H, W, topk_idx, topk_logit, mask, nullptr, nullptr, N, d, V, K, chunk,
+                    out_loss, nullptr, nullptr, row_kl, row_lse, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+            const uint8_t* mask, const float* row_lse, const float* grad_loss, int64_t N, int64_t d, int64_t V,
+            int64_t K, int64_t chunk, void* dH, float* dW, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return CKL_EINVAL;
+  try {
+    return run_impl(PASS_BWD, to_dt(dtype), H, W, topk_idx, topk_logit, mask, row_lse, grad_loss, N, d, V, K, chunk,
+                    nullptr, dH, dW, nullptr, nullptr, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_plan_pass(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk,
+                  uint64_t budget_bytes, int64_t* chunk_out, uint64_t* workspace_bytes_out) {
+  if (!dtype_ok(dtype)) return CKL_EINVAL;
+  if (pass != CKL_PASS_FUSED && pass != CKL_PASS_FWD && pass != CKL_PASS_BWD) return CKL_EINVAL;
   try {
     Layout L;
-    const int st = plan_impl(N, d, V, K, chunk, budget_bytes, dtype == CKL_DTYPE_BF16 ? 2 : 4, &L);
+    const int st = plan_impl((Pass)pass, N, d, V, K, chunk, budget_bytes, dtype == CKL_DTYPE_BF16 ? 2 : 4, &L);
     if (st != CKL_OK) return st;
     if (chunk_out) *chunk_out = L.C;
     if (workspace_bytes_out) *workspace_bytes_out = L.total;
@@ -325,6 +374,11 @@ int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chun
   } catch (...) {
     return CKL_EINVAL;
   }
+}
+
+int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
+             int64_t* chunk_out, uint64_t* workspace_bytes_out) {
+  return ckl_plan_pass(CKL_PASS_FUSED, N, d, V, K, dtype, chunk, budget_bytes, chunk_out, workspace_bytes_out);
 }
 
 void ckl_release_workspace(void) {

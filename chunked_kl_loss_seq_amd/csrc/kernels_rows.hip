@@ -160,17 +160,24 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
   const Scalars* sc = (const Scalars*)a.scal;
   const float scale = sc ? sc->scale : a.scale_value;
   const bool valid = a.mask == nullptr || a.mask[r] != 0;
-  const float w = valid ? scale : 0.f;
+  const float w = valid ? (a.gscale ? scale * *a.gscale : scale) : 0.f;
   float2* prow = a.part + r * a.n_slices;
 
-  // student log-normaliser from the slice pairs
-  float m = -INFINITY, s = 0.f;
-  for (int p = tid; p < a.n_slices; p += NT) {
-    const float2 q = prow[p];
-    lse_merge(m, s, q.x, q.y);
+  // student log-normaliser: merged from the slice pairs, or the value a
+  // forward pass over the same inputs saved (bitwise the same: the logits
+  // GEMM and the merge order do not depend on the chunking)
+  float lse;
+  if (a.lse_in) {
+    lse = a.lse_in[r];
+  } else {
+    float m = -INFINITY, s = 0.f;
+    for (int p = tid; p < a.n_slices; p += NT) {
+      const float2 q = prow[p];
+      lse_merge(m, s, q.x, q.y);
+    }
+    block_lse_merge<NT>(m, s, red);
+    lse = m + logf(s);
   }
-  block_lse_merge<NT>(m, s, red);
-  const float lse = m + logf(s);
 
   // teacher softmax over the cached logits; gather; KL; exact values at the ids
   const T* P = (const T*)a.P;
@@ -225,8 +232,8 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
     prow[p].y = valid ? w * __expf(q.x - lse) : 0.f;
   }
   if (tid == 0) {
-    a.kl_out[r] = valid ? kl : 0.f;
-    a.lse_out[r] = lse;
+    if (a.kl_out) a.kl_out[r] = valid ? kl : 0.f;
+    if (a.lse_out) a.lse_out[r] = lse;
   }
 }
 

@@ -58,6 +58,8 @@ struct RowArgs {
   int K;
   int64_t rows;
   float* scat;          // [rows, K] exact gradient values at the cached ids
+  const float* lse_in;  // [rows] log-normalisers saved by a forward pass, or null: merge the slice pairs
+  const float* gscale;  // device scalar multiplying the gradient, or null for 1
   float* kl_out;        // [rows] KL (0 for masked rows)
   float* lse_out;       // [rows]
   float* zg_dbg;        // optional [rows, K]

@@ -57,6 +57,9 @@ WORKLOADS = {
     4: Workload("gpt-oss-head-32k", 32768, 2880, 201088, 100, "bf16", 0, "zipf", 3.0, "none"),
     5: Workload("gpt-oss-head-4x32k", 131072, 2880, 201088, 100, "bf16", 0, "zipf", 3.0, "tailpad",
                 seq_len=32768),
+    # one 256K-token sequence: the pages' long-context point (memory stays
+    # almost flat as the input grows), at the gpt-oss head's shape
+    6: Workload("gpt-oss-head-256k", 262144, 2880, 201088, 100, "bf16", 0, "zipf", 3.0, "none"),
 }
 
 

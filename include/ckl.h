@@ -94,6 +94,40 @@ int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_
                    const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
                    float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream);
 
+/* The two-pass form of the same loss, for a training code whose backward runs
+ * apart from its forward: the forward keeps one number per position and the
+ * backward recomputes each chunk's logits from H and W instead of storing them
+ * ("A New Trick Slashes the Cost of Shrinking Giant AI Models", section "What
+ * did the researchers change?": chunks are computed and discarded, and what the
+ * backward pass needs is recomputed; the same page's table lists a
+ * forward-chunked loss beside the fused one).  Together the two calls do four
+ * d x V contractions per position instead of the fused call's three.
+ *
+ * ckl_fwd: loss and per-position log-normaliser, no gradients.
+ *   dtype      ckl_dtype of H and W
+ *   H, W, topk_idx, topk_logit, mask, N, d, V, K, chunk   as for ckl_fwd_bwd
+ *   out_loss   fp32 device scalar
+ *   row_lse    fp32 [N] (required)   logsumexp of each position's student logits
+ *   row_kl     fp32 [N] or NULL      KL_r (0 for masked positions)
+ * With the same inputs and chunk, loss, row_lse and row_kl are bitwise equal
+ * to those of ckl_fwd_bwd_ex. */
+int ckl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+            const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
+            float* row_lse, float* row_kl, hipStream_t stream);
+
+/* ckl_bwd: dH and dW of `grad_loss` x loss, recomputing every chunk's logits.
+ *   row_lse    fp32 [N] (required)   the values ckl_fwd wrote for these inputs
+ *   grad_loss  fp32 device scalar multiplying both gradients, or NULL for 1
+ *   dH         [N, d] in dtype (overwritten);  dW  fp32 [V, d] (overwritten)
+ * The log-normaliser is read from row_lse rather than recomputed.  With
+ * grad_loss NULL and the same chunk, dH and dW are bitwise equal to those of
+ * ckl_fwd_bwd. */
+int ckl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
+            const uint8_t* mask, const float* row_lse, const float* grad_loss, int64_t N, int64_t d, int64_t V,
+            int64_t K, int64_t chunk, void* dH, float* dW, hipStream_t stream);
+
+typedef enum { CKL_PASS_FUSED = 0, CKL_PASS_FWD = 1, CKL_PASS_BWD = 2 } ckl_pass;
+
 /* Chunk planner (pure host computation, needs no GPU).  The sequence is cut
  * into chunks of C rows so that the loss's own device memory stays bounded
  * independently of N ("A New Trick...", section "Does this matter for longer
@@ -106,6 +140,11 @@ int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_
  *                 call will allocate for its workspace */
 int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
              int64_t* chunk_out, uint64_t* workspace_bytes_out);
+
+/* ckl_plan for one of the calls: pass = ckl_pass (fused = ckl_plan; the
+ * forward-only call needs no dH split-K slabs, so it can take longer chunks). */
+int ckl_plan_pass(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk,
+                  uint64_t budget_bytes, int64_t* chunk_out, uint64_t* workspace_bytes_out);
 
 /* Frees every cached workspace (after synchronising the device). */
 void ckl_release_workspace(void);
@@ -131,11 +170,12 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
                    int64_t V, int64_t K, float scale, int g_bf16, float* zg_out, int32_t* scatter_ids_out,
                    void* G_out, float* kl_out, float* lse_out, hipStream_t stream);
 
-/* Measurement support.  While enabled, every kernel launch of a fwd_bwd call
- * is bracketed by HIP events on the call's stream.  ckl_timing_query waits for
- * the recorded events and returns the summed milliseconds and launch count of
- * one kernel kind: 0 logits GEMM, 1 row pass, 2 dH GEMM, 3 dH split reduce,
- * 4 dW GEMM, 5 other.  Not for concurrent use from several threads. */
+/* Measurement support.  While enabled, every kernel launch of a loss call
+ * (ckl_fwd_bwd*, ckl_fwd, ckl_bwd) is bracketed by HIP events on the call's
+ * stream.  ckl_timing_query waits for the recorded events and returns the
+ * summed milliseconds and launch count of one kernel kind: 0 logits GEMM,
+ * 1 row pass, 2 dH GEMM, 3 dH split reduce, 4 dW GEMM, 5 other.  Not for
+ * concurrent use from several threads. */
 int ckl_timing_enable(int on);
 int ckl_timing_query(int kind, double* total_ms, int64_t* launches);
 

@@ -132,3 +132,40 @@ def test_timing_query_argument_check():
     n = ctypes.c_int64(0)
     assert L.ckl_timing_query(99, ctypes.byref(t), ctypes.byref(n)) == -1
     assert B.timing_enable(False) is None
+
+
+def test_plan_per_pass():
+    # the backward needs the same workspace as the fused call; the forward
+    # alone has no dH split-K slabs, so at equal chunk it is exactly that much
+    # smaller, and the planner can give it longer chunks
+    for (N, d, V, K, C) in [(4096, 2048, 32000, 100, 1024), (600, 200, 1003, 37, 256)]:
+        cf, wf = B.plan(N, d, V, K, chunk=C)
+        cb, wb = B.plan(N, d, V, K, chunk=C, pass_="bwd")
+        c1, w1 = B.plan(N, d, V, K, chunk=C, pass_="fwd")
+        assert cf == cb == c1 == min(C, N)
+        assert wb == wf
+        assert w1 == ws_formula(N, d, V, K, c1, 0)
+    c_fused, _ = B.plan(32768, 2880, 201088, 100)
+    c_fwd, w_fwd = B.plan(32768, 2880, 201088, 100, pass_="fwd")
+    assert w_fwd <= 6 * GiB and c_fwd >= c_fused
+    L = B.lib()
+    c = ctypes.c_int64(0)
+    b = ctypes.c_uint64(0)
+    assert L.ckl_plan_pass(3, 64, 8, 10, 2, 0, 0, 0, ctypes.byref(c), ctypes.byref(b)) == -1
+
+
+def test_fwd_and_bwd_reject_bad_arguments_before_any_gpu_call():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = vp(1 << 20)
+    z = vp(0)
+    # forward: row_lse is required, out_loss is required
+    assert L.ckl_fwd(0, good, good, good, good, z, 4, 8, 10, 2, 0, good, z, z, z) == -1
+    assert L.ckl_fwd(0, good, good, good, good, z, 4, 8, 10, 2, 0, z, good, z, z) == -1
+    assert L.ckl_fwd(5, good, good, good, good, z, 4, 8, 10, 2, 0, good, good, z, z) == -1
+    assert L.ckl_fwd(0, good, good, good, good, z, 4, 12, 10, 2, 0, good, good, z, z) == -5
+    # backward: the saved row_lse, dH and dW are required; a misaligned grad_loss is rejected
+    assert L.ckl_bwd(0, good, good, good, good, z, z, z, 4, 8, 10, 2, 0, good, good, z) == -1
+    assert L.ckl_bwd(0, good, good, good, good, z, good, z, 4, 8, 10, 2, 0, z, good, z) == -1
+    assert L.ckl_bwd(0, good, good, good, good, z, good, vp((1 << 20) + 2), 4, 8, 10, 2, 0, good, good, z) == -1
+    assert L.ckl_bwd(0, good, good, good, good, z, good, z, 4, 8, 10, 11, 0, good, good, z) == -1

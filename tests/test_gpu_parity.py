@@ -304,3 +304,9 @@ def test_gpt_oss_head_workload_sampled():
 def test_gpt_oss_head_long_batch_workload_sampled():
     binding = _need_gpu()
     _sampled_full_size(binding, 5)
+
+
+def test_gpt_oss_head_256k_sequence_workload_sampled():
+    # one 262,144-token sequence: 32 chunks under the same 6 GiB workspace
+    binding = _need_gpu()
+    _sampled_full_size(binding, 6)

@@ -73,3 +73,13 @@ def test_zipf_ids_skewed_and_distinct():
     # id 0 is the most likely draw and appears in nearly every row
     assert counts[0] == counts.max() and counts[0] > 0.9 * 512
     assert counts[:100].sum() > counts[100:].sum() * 0.3
+
+
+def test_long_sequence_recipe():
+    wl = WL.WORKLOADS[6]
+    assert (wl.N, wl.d, wl.V, wl.K, wl.mask) == (262144, 2880, 201088, 100, "none")
+    a = WL.make(6, rows=128)
+    assert a["H"].shape == (128, 2880) and a["ids"].shape == (128, 100)
+    assert np.all(a["mask"] == 1)
+    assert all(len(set(r)) == 100 for r in a["ids"].tolist())
+    assert np.all(np.diff(a["tlogit"], axis=1) <= 0)
