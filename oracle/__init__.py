@@ -8,3 +8,4 @@ from .kl_oracle import (  # noqa: F401
     kl_dense,
     kl_rows,
 )
+from .topk_oracle import topk_rows  # noqa: F401,E402
