@@ -123,6 +123,69 @@ def cpu_baseline(number, rows):
                       f"{dt:.2f} s wall"}
 
 
+def bench_topk(args):
+    """Teacher cache writer: per row of bf16 teacher logits [R, V], the top K ids and values."""
+    import numpy as np  # noqa: F401
+    import torch
+
+    from chunked_kl_loss_seq_amd import binding
+    from chunked_kl_loss_seq_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    binding.lib()
+    R, V, K = args.topk_rows, 201088, 100
+    log(f"[bench] generating {R} x {V} bf16 teacher logits (N(0, 3))")
+    x = torch.from_numpy(WL.teacher_logits(R, V, seed=1)).to("cuda:0").to(torch.bfloat16).contiguous()
+    ids = torch.empty((R, K), dtype=torch.int32, device=x.device)
+    vals = torch.empty((R, K), dtype=torch.float32, device=x.device)
+    for _ in range(args.warmup):
+        binding.topk(x, K, ids, vals)
+    torch.cuda.synchronize()
+    binding.timing_enable(True)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        binding.topk(x, K, ids, vals)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    k_ms, k_n = binding.timing_query("topk")
+    binding.timing_enable(False)
+    launch_ms = k_ms / max(k_n, 1)
+    alg_bytes = R * V * 2 + R * K * 8  # logits read once, ids and values written once
+    gbs = alg_bytes / (launch_ms / 1e3) / 1e9
+    log(f"[bench] top-K: {ms:.3f} ms/step, {R / (ms / 1e3):.0f} rows/s, {gbs:.0f} GB/s algorithmic")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import topk_rows
+
+        n = 256
+        xs = x[:n].float().cpu().numpy()
+        t0 = time.perf_counter()
+        topk_rows(xs, K)
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} rows, float64 NumPy stable argsort per row, {dt:.2f} s wall"}
+        log(f"[bench] oracle {cpu['value']:.1f} rows/s")
+    out = {
+        "metric": "teacher top-K cache writer rows/s (HBM-bound)",
+        "value": round(R / (ms / 1e3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "teacher-logits-gpt-oss-vocab", "rows": R, "V": V, "K": K, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "top-K",
+                     "launch_avg_ms": round(launch_ms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,8 +193,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="named workload number (4 = gpt-oss head, 32K tokens)")
     ap.add_argument("--chunk", type=int, default=-1, help="rows per chunk (default: the workload's own)")
-    ap.add_argument("--variant", choices=["fused", "two-pass"], default="fused",
-                    help="fused: one ckl_fwd_bwd call per step; two-pass: ckl_fwd then ckl_bwd (logits recomputed)")
+    ap.add_argument("--variant", choices=["fused", "two-pass", "topk"], default="fused",
+                    help="fused: one ckl_fwd_bwd call per step; two-pass: ckl_fwd then ckl_bwd (logits recomputed); "
+                         "topk: the teacher top-K cache writer (ckl_topk) over --topk-rows rows")
+    ap.add_argument("--topk-rows", type=int, default=8192, help="rows of teacher logits for --variant topk")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="positions in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -161,6 +226,9 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    if args.variant == "topk":
+        bench_topk(args)
+        return
 
     import numpy as np
     import torch

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     recompute_kl,
     release_workspace,
     timing_enable,
+    topk,
     timing_query,
     workspace_bytes_held,
 )

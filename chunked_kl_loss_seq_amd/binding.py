@@ -16,7 +16,7 @@ CKL_OK = 0
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 PASSES = {"fused": 0, "fwd": 1, "bwd": 2}
-TIMING_KINDS = {"logits": 0, "rows": 1, "dh": 2, "dh_reduce": 3, "dw": 4, "other": 5}
+TIMING_KINDS = {"logits": 0, "rows": 1, "dh": 2, "dh_reduce": 3, "dw": 4, "other": 5, "topk": 6}
 
 _lib = None
 
@@ -50,6 +50,8 @@ def lib():
     L.ckl_fwd.restype = ctypes.c_int
     L.ckl_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp]
     L.ckl_bwd.restype = ctypes.c_int
+    L.ckl_topk.argtypes = [ctypes.c_int, vp, i64, i64, i64, vp, vp, vp]
+    L.ckl_topk.restype = ctypes.c_int
     L.ckl_release_workspace.argtypes = []
     L.ckl_release_workspace.restype = None
     L.ckl_workspace_bytes_held.argtypes = []
@@ -201,6 +203,28 @@ def bwd(H, W, ids, tlogit, row_lse, mask=None, grad_loss=None, chunk=0, dH=None,
                        _ptr(grad_loss), N, d, V, K, int(chunk), _ptr(dH), _ptr(dW), _stream(torch, H.device))
     _check(st, "ckl_bwd")
     return dH, dW
+
+
+def topk(logits, K, ids_out=None, vals_out=None):
+    """Teacher cache writer: (ids int32 [N,K], values float32 [N,K]) of the K largest
+    logits per row of a contiguous bf16 or fp32 GPU tensor [N,V], by value
+    descending, equal values by id ascending."""
+    import torch
+
+    if not logits.is_cuda or not logits.is_contiguous() or logits.dim() != 2:
+        raise ValueError("topk needs a contiguous 2-D GPU tensor")
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be bfloat16 or float32")
+    N, V = logits.shape
+    dt = DTYPE_BF16 if logits.dtype == torch.bfloat16 else DTYPE_F32
+    if ids_out is None:
+        ids_out = torch.empty((N, K), dtype=torch.int32, device=logits.device)
+    if vals_out is None:
+        vals_out = torch.empty((N, K), dtype=torch.float32, device=logits.device)
+    st = lib().ckl_topk(dt, _ptr(logits), N, V, int(K), _ptr(ids_out), _ptr(vals_out),
+                        _stream(torch, logits.device))
+    _check(st, "ckl_topk")
+    return ids_out, vals_out
 
 
 def debug_rows(Z, ids, tlogit, mask=None, scale=1.0, g_bf16=True):

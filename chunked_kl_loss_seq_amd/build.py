@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libckl.so")
-SOURCES = ["ckl_api.hip", "kernels_gemm.hip", "kernels_rows.hip"]
+SOURCES = ["ckl_api.hip", "kernels_gemm.hip", "kernels_rows.hip", "kernels_topk.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -159,7 +159,7 @@ int get_workspace(int dev, hipStream_t s, uint64_t bytes, void** ptr) {
 }
 
 // ------------------------------------------------------------------ timing
-enum Kind { T_LOGITS = 0, T_ROWS, T_DH, T_DHRED, T_DW, T_OTHER, T_KINDS };
+enum Kind { T_LOGITS = 0, T_ROWS, T_DH, T_DHRED, T_DW, T_OTHER, T_TOPK, T_KINDS };
 struct TimingState {
   bool on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
@@ -355,6 +355,23 @@ int ckl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, co
   try {
     return run_impl(PASS_BWD, to_dt(dtype), H, W, topk_idx, topk_logit, mask, row_lse, grad_loss, N, d, V, K, chunk,
                     nullptr, dH, dW, nullptr, nullptr, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_topk(int dtype, const void* logits, int64_t N, int64_t V, int64_t K, int32_t* ids_out, float* vals_out,
+             hipStream_t stream) {
+  if (!dtype_ok(dtype)) return CKL_EINVAL;
+  const size_t esz = dtype == CKL_DTYPE_BF16 ? 2 : 4;
+  if (!logits || !ids_out || !vals_out) return CKL_EINVAL;
+  if (!aligned(logits, esz) || !aligned(ids_out, 4) || !aligned(vals_out, 4)) return CKL_EINVAL;
+  if (N <= 0 || V <= 0 || K <= 0 || K > V) return CKL_EINVAL;
+  if (K > kMaxK || V > 0x7FFFFFFFll || N > (int64_t)(0xFFFFFFFFull / 512)) return CKL_EUNSUPPORTED;
+  try {
+    Timed t(T_TOPK, stream);
+    CKL_TRY(launch_topk(to_dt(dtype), logits, N, V, K, ids_out, vals_out, stream));
+    return CKL_OK;
   } catch (...) {
     return CKL_EHIP;
   }

@@ -1,0 +1,301 @@
+// Offline top-K cache writer: per row of teacher logits, the K largest values
+// and their ids, by value descending and equal values by id ascending.
+//
+// The teacher runs once and only its K most likely predictions per position
+// are stored ("A New Trick Slashes the Cost of Shrinking Giant AI Models",
+// section "What did the researchers change?"; "Making Knowledge Distillation
+// Cheap Enough to Run at Scale" (elseif.net), offline-cache paragraph).  The
+// pages do not order equal logits; the order taken here is the stable one
+// (lower id first), which makes the result unique.
+//
+// One workgroup per row, bound by reading the row (2 or 4 bytes per logit).
+// Values are compared through an order-preserving unsigned key of their bits
+// (-0 is keyed as +0; NaN is outside the supported inputs):
+//  1. every thread takes the largest key of its strided share of the row;
+//  2. t0 = the lower edge of the histogram bin (top 12 key bits) in which,
+//     counting the maxima from the top, the K-th one falls; those K maxima
+//     are K distinct elements, so at least K keys are >= t0;
+//  3. the elements with key >= t0 are collected into LDS as (key, id) pairs
+//     (a second read of the row, mostly served by the caches);
+//  4. ordered by (key descending, id ascending): each pair's place is the
+//     number of larger pairs (a bitonic sort when more pairs than threads).
+// When more than kCap elements reach t0 (many equal values near the top) or
+// K exceeds the thread count, an exact path takes over: a binary search over
+// the key range finds the K-th largest key T, the elements above T are
+// collected, and the elements equal to T are taken in id order with one
+// block-wide scan per run of ids until K are held.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace ckl {
+
+namespace {
+
+constexpr int kTopkThreads = 512;
+constexpr int kCap = 4096;  // (key, id) pairs held in LDS
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+
+template <typename T>
+struct Key;
+template <>
+struct Key<__bf16> {
+  static constexpr int kBits = 16;
+  __device__ static inline uint32_t of(__bf16 v) {
+    uint32_t b = __builtin_bit_cast(uint16_t, v);
+    if (b == 0x8000u) b = 0;
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  }
+};
+template <>
+struct Key<float> {
+  static constexpr int kBits = 32;
+  __device__ static inline uint32_t of(float v) {
+    uint32_t b = __builtin_bit_cast(uint32_t, v);
+    if (b == 0x80000000u) b = 0;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+};
+
+// (key, id) packed so that a larger number means an earlier place in the
+// answer: key descending, then id ascending.
+__device__ inline uint64_t pack(uint32_t key, uint32_t id) { return ((uint64_t)key << 32) | (0xFFFFFFFFu - id); }
+__device__ inline uint32_t unpack_id(uint64_t c) { return 0xFFFFFFFFu - (uint32_t)c; }
+
+// Sort a[0, n) descending (n a power of two), all threads of the block.
+__device__ inline void bitonic_desc(uint64_t* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kTopkThreads) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint64_t x = a[i], y = a[l];
+          const bool first_half_desc = (i & k) == 0;
+          if (first_half_desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ inline uint32_t block_sum(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkThreads / 64; ++i) t += red[i];
+  return t;
+}
+
+// Sum of v over the threads after this one (thread order).
+__device__ inline uint32_t block_suffix_excl(uint32_t v, uint32_t* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t x = v;  // becomes the sum over lanes >= lane of this wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(x, o);
+    if (lane + o < 64) x += y;
+  }
+  __syncthreads();
+  if (lane == 0) red[w] = x;
+  __syncthreads();
+  uint32_t later = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkThreads / 64; ++i) later += i > w ? red[i] : 0;
+  return later + x - v;
+}
+
+// Exclusive rank of this thread's flag among the block's set flags (thread
+// order) and the total number set.
+__device__ inline uint32_t block_rank(bool f, uint32_t* red, uint32_t* total) {
+  const uint64_t bal = __ballot(f);
+  const uint32_t in_wave = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = (uint32_t)__popcll(bal);
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkThreads / 64; ++i) {
+    before += i < w ? red[i] : 0;
+    all += red[i];
+  }
+  *total = all;
+  return before + in_wave;
+}
+
+// Visit every element of a row as (key, id): 16-byte loads when the row is
+// 16-byte aligned and a whole number of 16-byte chunks (then many loads per
+// thread are in flight at once), element loads otherwise.
+template <typename T, typename F>
+__device__ inline void for_each_key(const T* row, int64_t V, bool vec, F&& fn) {
+  if (vec) {
+    constexpr int EPC = 16 / (int)sizeof(T);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* p = (const u32x4*)row;
+    const int64_t chunks = V / EPC;
+#pragma unroll 4
+    for (int64_t c = threadIdx.x; c < chunks; c += kTopkThreads) {
+      const u32x4 v = p[c];
+      const T* e = (const T*)&v;
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) fn(Key<T>::of(e[i]), c * EPC + i);
+    }
+  } else {
+#pragma unroll 8
+    for (int64_t e = threadIdx.x; e < V; e += kTopkThreads) fn(Key<T>::of(row[e]), e);
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict__ x, int64_t V, int K,
+                                                           int32_t* __restrict__ ids_out,
+                                                           float* __restrict__ vals_out) {
+  __shared__ uint64_t cand[kCap];
+  __shared__ uint32_t red[kTopkThreads / 64];
+  __shared__ uint32_t count, t0_s;
+  const int tid = threadIdx.x;
+  const T* row = x + (int64_t)blockIdx.x * V;
+  const bool vec = ((uintptr_t)row % 16 == 0) && ((V * (int64_t)sizeof(T)) % 16 == 0);
+
+  bool exact = K > kTopkThreads;
+  uint32_t n_held = 0;
+  if (!exact) {
+    // 1. largest key of this thread's share
+    uint32_t mk = 0;
+    for_each_key(row, V, vec, [&](uint32_t k, int64_t) { mk = max(mk, k); });
+    // 2. t0 = the lower edge of the histogram bin (top 12 key bits) of the
+    //    maxima where, counting from the top, K maxima are reached: at least
+    //    K maxima, so K distinct elements, have key >= t0
+    uint32_t* hist = (uint32_t*)cand;  // free until the candidates are collected
+    constexpr int kShift = Key<T>::kBits - kHistBits;
+    for (int i = tid; i < kHistBins; i += kTopkThreads) hist[i] = 0;
+    if (tid == 0) count = 0;
+    __syncthreads();
+    atomicAdd(&hist[mk >> kShift], 1u);
+    __syncthreads();
+    constexpr int kPer = kHistBins / kTopkThreads;  // bins per thread, thread t owns [kPer t, kPer t + kPer)
+    uint32_t mine = 0;
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) mine += hist[kPer * tid + b];
+    const uint32_t above = block_suffix_excl(mine, red);  // maxima in the bins of higher threads
+    if (above < (uint32_t)K && above + mine >= (uint32_t)K) {
+      uint32_t c = above;
+      for (int b = kPer - 1; b >= 0; --b) {
+        c += hist[kPer * tid + b];
+        if (c >= (uint32_t)K) {
+          t0_s = (uint32_t)(kPer * tid + b) << kShift;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t t0 = t0_s;
+    // 3. every element with key >= t0
+    for_each_key(row, V, vec, [&](uint32_t k, int64_t e) {
+      if (k >= t0) {
+        const uint32_t slot = atomicAdd(&count, 1u);
+        if (slot < (uint32_t)kCap) cand[slot] = pack(k, (uint32_t)e);
+      }
+    });
+    __syncthreads();
+    n_held = count;
+    // every thread has read the count before the exact path may reset it
+    __syncthreads();
+    exact = n_held > (uint32_t)kCap;
+  }
+
+  int n = K;
+  if (!exact) {
+    n = (int)n_held;
+  } else {
+    // exact path: T = the K-th largest key, by binary search over the key range
+    uint64_t lo = 0, hi = (Key<T>::kBits == 32) ? 0xFFFFFFFFull : 0xFFFFull;
+    while (lo < hi) {
+      const uint64_t mid = lo + (hi - lo + 1) / 2;
+      uint32_t c = 0;
+      for (int64_t e = tid; e < V; e += kTopkThreads) c += Key<T>::of(row[e]) >= (uint32_t)mid;
+      if (block_sum(c, red) >= (uint32_t)K)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const uint32_t T0 = (uint32_t)lo;
+    if (tid == 0) count = 0;
+    __syncthreads();
+    // the elements above T (fewer than K of them)
+    for (int64_t e = tid; e < V; e += kTopkThreads) {
+      const uint32_t k = Key<T>::of(row[e]);
+      if (k > T0) cand[atomicAdd(&count, 1u)] = pack(k, (uint32_t)e);
+    }
+    __syncthreads();
+    const uint32_t above = count;
+    // the elements equal to T, lowest ids first, until K are held
+    uint32_t taken = 0, need = (uint32_t)K - above;
+    for (int64_t base = 0; need > 0 && base < V; base += kTopkThreads) {
+      const int64_t e = base + tid;
+      const bool f = e < V && Key<T>::of(row[e]) == T0;
+      uint32_t total = 0;
+      const uint32_t rank = block_rank(f, red, &total);
+      if (f && rank < need) cand[above + taken + rank] = pack(T0, (uint32_t)e);
+      const uint32_t got = total < need ? total : need;
+      taken += got;
+      need -= got;
+    }
+    __syncthreads();
+  }
+
+  // 4. order the held pairs and write the first K.  The packed pairs are
+  //    distinct, so a pair's place is the number of larger pairs: up to one
+  //    pair per thread that count is cheaper than a sort.
+  int32_t* io = ids_out + (int64_t)blockIdx.x * K;
+  float* vo = vals_out + (int64_t)blockIdx.x * K;
+  if (n <= kTopkThreads) {
+    if (tid < n) {
+      const uint64_t c = cand[tid];
+      int place = 0;
+      for (int i = 0; i < n; ++i) place += cand[i] > c;
+      if (place < K) {
+        const uint32_t id = unpack_id(c);
+        io[place] = (int32_t)id;
+        vo[place] = (float)row[id];
+      }
+    }
+    return;
+  }
+  int p2 = 1;
+  while (p2 < n) p2 <<= 1;
+  for (int i = n + tid; i < p2; i += kTopkThreads) cand[i] = 0;  // below every real pair
+  __syncthreads();
+  bitonic_desc(cand, p2);
+  for (int k = tid; k < K; k += kTopkThreads) {
+    const uint32_t id = unpack_id(cand[k]);
+    io[k] = (int32_t)id;
+    vo[k] = (float)row[id];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(Dtype dt, const void* x, int64_t N, int64_t V, int64_t K, int32_t* ids, float* vals,
+                       hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(topk_kernel<__bf16>, dim3((unsigned)N), dim3(kTopkThreads), 0, s, (const __bf16*)x, V,
+                       (int)K, ids, vals);
+  else
+    hipLaunchKernelGGL(topk_kernel<float>, dim3((unsigned)N), dim3(kTopkThreads), 0, s, (const float*)x, V, (int)K,
+                       ids, vals);
+  return hipGetLastError();
+}
+
+}  // namespace ckl

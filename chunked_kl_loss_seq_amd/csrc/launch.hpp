@@ -40,6 +40,11 @@ int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V);
 // tile width used along d by the dH and dW contractions.
 int d_tile(Dtype dt, int64_t d);
 
+// Per row of x [N, V] (bf16 or fp32), the K largest values and their ids, by
+// value descending and equal values by id ascending (see kernels_topk.hip).
+hipError_t launch_topk(Dtype dt, const void* x, int64_t N, int64_t V, int64_t K, int32_t* ids, float* vals,
+                       hipStream_t s);
+
 // Valid-token count n and scale 1/n (0 if n = 0) into scal (int64 n, float s).
 hipError_t launch_mask_count(const uint8_t* mask, int64_t N, void* scal, hipStream_t s);
 

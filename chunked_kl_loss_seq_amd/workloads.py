@@ -31,7 +31,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make", "make_custom", "round_bf16", "bf16_bits"]
+__all__ = ["Workload", "WORKLOADS", "make", "make_custom", "round_bf16", "bf16_bits", "teacher_logits"]
 
 
 @dataclass(frozen=True)
@@ -263,3 +263,27 @@ def small(N, d, V, K, dtype="bf16", ids="uniform", tstd=3.0, mask="none", seed=0
     """An ad-hoc workload of any shape, drawn by the same recipe."""
     wl = Workload(f"custom-{N}x{d}x{V}x{K}", N, d, V, K, dtype, 0, ids, tstd, mask, seq_len=seq_len)
     return make_custom(wl, seed)
+
+
+def teacher_logits(N, V, std=3.0, seed=0, bf16=True, rows=None):
+    """Full-vocabulary teacher logit rows [N, V] for the top-K cache writer:
+    N(0, std) drawn in fp32 (rounded RNE to bf16 when ``bf16``), in blocks of
+    256 rows from the children of SeedSequence(seed), so the first ``rows``
+    rows do not depend on N.  bf16 rounding leaves many equal values, which
+    exercises the tie order."""
+    n = N if rows is None else min(rows, N)
+    ss = np.random.SeedSequence(seed)
+    if n == N:
+        return _normal(ss, (N, V), std, bf16, block_rows=256)
+    # the first blocks only: same children, same draws
+    full_blocks = (N + 255) // 256
+    kids = ss.spawn(full_blocks)
+    need = (n + 255) // 256
+    out = np.empty((need * 256, V), dtype=np.float32)
+    for b in range(need):
+        r1 = min(N, (b + 1) * 256)
+        blk = np.random.default_rng(kids[b]).standard_normal((r1 - b * 256, V), dtype=np.float32)
+        if std != 1.0:
+            blk *= np.float32(std)
+        out[b * 256:r1] = round_bf16(blk) if bf16 else blk
+    return out[:n]

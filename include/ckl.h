@@ -128,6 +128,22 @@ int ckl_bwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, co
 
 typedef enum { CKL_PASS_FUSED = 0, CKL_PASS_FWD = 1, CKL_PASS_BWD = 2 } ckl_pass;
 
+/* Offline top-K cache writer: the step that produces topk_idx / topk_logit from
+ * the teacher's logits, run once per training corpus ("A New Trick...",
+ * section "What did the researchers change?": the teacher is run once and only
+ * its top 100 predictions per position are saved; elseif.net page,
+ * offline-cache paragraph).
+ *   dtype     ckl_dtype of logits
+ *   logits    [N, V] row-major, bf16 or fp32 (2- or 4-byte aligned); no NaN
+ *   ids_out   int32 [N, K]   token ids of the K largest logits of each row
+ *   vals_out  fp32 [N, K]    those logits (exact conversion of the inputs)
+ * Each row's K pairs are ordered by value descending; equal values (-0 equals
+ * +0) by id ascending, so the result is unique.  1 <= K <= min(V, 2048),
+ * V < 2^31.  Enqueued on `stream`; no workspace.  Errors as for the other
+ * calls; nothing is enqueued on an error. */
+int ckl_topk(int dtype, const void* logits, int64_t N, int64_t V, int64_t K, int32_t* ids_out, float* vals_out,
+             hipStream_t stream);
+
 /* Chunk planner (pure host computation, needs no GPU).  The sequence is cut
  * into chunks of C rows so that the loss's own device memory stays bounded
  * independently of N ("A New Trick...", section "Does this matter for longer
@@ -171,11 +187,11 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
                    void* G_out, float* kl_out, float* lse_out, hipStream_t stream);
 
 /* Measurement support.  While enabled, every kernel launch of a loss call
- * (ckl_fwd_bwd*, ckl_fwd, ckl_bwd) is bracketed by HIP events on the call's
+ * (ckl_fwd_bwd*, ckl_fwd, ckl_bwd, ckl_topk) is bracketed by HIP events on the call's
  * stream.  ckl_timing_query waits for the recorded events and returns the
  * summed milliseconds and launch count of one kernel kind: 0 logits GEMM,
- * 1 row pass, 2 dH GEMM, 3 dH split reduce, 4 dW GEMM, 5 other.  Not for
- * concurrent use from several threads. */
+ * 1 row pass, 2 dH GEMM, 3 dH split reduce, 4 dW GEMM, 5 other, 6 top-K
+ * (ckl_topk).  Not for concurrent use from several threads. */
 int ckl_timing_enable(int on);
 int ckl_timing_query(int kind, double* total_ms, int64_t* launches);
 

@@ -169,3 +169,17 @@ def test_fwd_and_bwd_reject_bad_arguments_before_any_gpu_call():
     assert L.ckl_bwd(0, good, good, good, good, z, good, z, 4, 8, 10, 2, 0, z, good, z) == -1
     assert L.ckl_bwd(0, good, good, good, good, z, good, vp((1 << 20) + 2), 4, 8, 10, 2, 0, good, good, z) == -1
     assert L.ckl_bwd(0, good, good, good, good, z, good, z, 4, 8, 10, 11, 0, good, good, z) == -1
+
+
+def test_topk_rejects_bad_arguments_before_any_gpu_call():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = vp(1 << 20)
+    z = vp(0)
+    assert L.ckl_topk(0, z, 4, 10, 2, good, good, z) == -1          # null logits
+    assert L.ckl_topk(0, good, 4, 10, 2, z, good, z) == -1          # null ids
+    assert L.ckl_topk(1, vp((1 << 20) + 2), 4, 10, 2, good, good, z) == -1  # fp32 logits misaligned
+    assert L.ckl_topk(0, good, 4, 10, 11, good, good, z) == -1      # K > V
+    assert L.ckl_topk(0, good, 0, 10, 2, good, good, z) == -1       # N = 0
+    assert L.ckl_topk(0, good, 4, 5000, 3000, good, good, z) == -5  # K > 2048
+    assert L.ckl_topk(9, good, 4, 10, 2, good, good, z) == -1       # unknown dtype

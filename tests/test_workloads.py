@@ -83,3 +83,14 @@ def test_long_sequence_recipe():
     assert np.all(a["mask"] == 1)
     assert all(len(set(r)) == 100 for r in a["ids"].tolist())
     assert np.all(np.diff(a["tlogit"], axis=1) <= 0)
+
+
+def test_teacher_logits_recipe():
+    a = WL.teacher_logits(600, 3000, seed=3)
+    b = WL.teacher_logits(600, 3000, seed=3, rows=300)
+    np.testing.assert_array_equal(a[:300], b)
+    assert np.all((a.view(np.uint32) & 0xFFFF) == 0)  # bf16-exact
+    assert abs(a.std() - 3.0) < 0.05
+    # bf16 rounding leaves equal values among the largest ones
+    top = np.sort(a, axis=1)[:, -100:]
+    assert np.mean([len(np.unique(r)) < 100 for r in top]) > 0.5
