@@ -33,9 +33,12 @@ namespace ckl {
 namespace {
 
 constexpr int kTopkThreads = 512;
-constexpr int kCap = 4096;  // (key, id) pairs held in LDS
+constexpr int kCap = 4096;  // (key, id) pairs held in LDS (at least the largest K)
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
+static_assert(kHistBins * 4 <= kCap * 8, "the histogram lives in the candidate store");
+static_assert(kHistBins % kTopkThreads == 0, "whole bins per thread");
+static_assert(kCap >= kMaxK, "the exact path holds K pairs");
 
 template <typename T>
 struct Key;
@@ -57,6 +60,62 @@ struct Key<float> {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   }
 };
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Element i of a 16-byte chunk, taken out by bit casts (no type punning
+// through pointers).
+__device__ inline __bf16 chunk_elem(const u32x4_t& v, int i, __bf16*) {
+  const uint32_t w = v[i >> 1];
+  return __builtin_bit_cast(__bf16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+__device__ inline float chunk_elem(const u32x4_t& v, int i, float*) {
+  const uint32_t w = v[i];  // a scalar first: bit-casting the subscript itself read lane 0
+  return __builtin_bit_cast(float, w);
+}
+
+// Largest value of a 16-byte chunk as fp32 (bf16 halves widened by a mask or
+// a shift: exact).  The streaming passes work on values, which costs about
+// one max instruction per element; keys are formed only for the threshold and
+// for the few elements that reach it.
+__device__ inline float chunk_max(const u32x4_t& v, __bf16*) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    const float hi = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    const float lo = __builtin_bit_cast(float, w << 16);
+    m = fmaxf(m, fmaxf(hi, lo));
+  }
+  return m;
+}
+__device__ inline float chunk_max(const u32x4_t& v, float*) {
+  const uint32_t a = v[0], b = v[1], c = v[2], d = v[3];
+  return fmaxf(fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)),
+               fmaxf(__builtin_bit_cast(float, c), __builtin_bit_cast(float, d)));
+}
+
+// Key of a value held exactly in fp32 (a widened bf16 or an fp32 element).
+template <typename T>
+__device__ inline uint32_t key_of_value(float v) {
+  if constexpr (sizeof(T) == 2)
+    return Key<__bf16>::of(__builtin_bit_cast(__bf16, (uint16_t)(__builtin_bit_cast(uint32_t, v) >> 16)));
+  else
+    return Key<float>::of(v);
+}
+
+// The value whose key is t, for t above the key of -inf (below it the bit
+// patterns are NaNs): the keys invert back to bit patterns.
+template <typename T>
+__device__ inline float value_of_key(uint32_t t) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t b = (t & 0x8000u) ? (t & 0x7FFFu) : (~t & 0xFFFFu);
+    return __builtin_bit_cast(float, b << 16);
+  } else {
+    const uint32_t b = (t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t;
+    return __builtin_bit_cast(float, b);
+  }
+}
 
 // (key, id) packed so that a larger number means an earlier place in the
 // answer: key descending, then id ascending.
@@ -140,15 +199,13 @@ template <typename T, typename F>
 __device__ inline void for_each_key(const T* row, int64_t V, bool vec, F&& fn) {
   if (vec) {
     constexpr int EPC = 16 / (int)sizeof(T);
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4* p = (const u32x4*)row;
+    const u32x4_t* p = (const u32x4_t*)row;
     const int64_t chunks = V / EPC;
 #pragma unroll 4
     for (int64_t c = threadIdx.x; c < chunks; c += kTopkThreads) {
-      const u32x4 v = p[c];
-      const T* e = (const T*)&v;
+      const u32x4_t v = p[c];
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) fn(Key<T>::of(e[i]), c * EPC + i);
+      for (int i = 0; i < EPC; ++i) fn(Key<T>::of(chunk_elem(v, i, (T*)nullptr)), c * EPC + i);
     }
   } else {
 #pragma unroll 8
@@ -171,8 +228,21 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
   uint32_t n_held = 0;
   if (!exact) {
     // 1. largest key of this thread's share
-    uint32_t mk = 0;
-    for_each_key(row, V, vec, [&](uint32_t k, int64_t) { mk = max(mk, k); });
+    uint32_t mk = 0;  // 0 is below every element's key: a thread with no element
+    if (vec) {
+      const u32x4_t* p = (const u32x4_t*)row;
+      const int64_t chunks = V / (16 / (int64_t)sizeof(T));
+      float mv = -INFINITY;
+      bool any = false;
+#pragma unroll 4
+      for (int64_t c = tid; c < chunks; c += kTopkThreads) {
+        mv = fmaxf(mv, chunk_max(p[c], (T*)nullptr));
+        any = true;
+      }
+      mk = any ? key_of_value<T>(mv) : 0u;
+    } else {
+      for_each_key(row, V, vec, [&](uint32_t k, int64_t) { mk = max(mk, k); });
+    }
     // 2. t0 = the lower edge of the histogram bin (top 12 key bits) of the
     //    maxima where, counting from the top, K maxima are reached: at least
     //    K maxima, so K distinct elements, have key >= t0
@@ -201,12 +271,31 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
     __syncthreads();
     const uint32_t t0 = t0_s;
     // 3. every element with key >= t0
-    for_each_key(row, V, vec, [&](uint32_t k, int64_t e) {
+    auto hold = [&](uint32_t k, int64_t e) {
       if (k >= t0) {
         const uint32_t slot = atomicAdd(&count, 1u);
         if (slot < (uint32_t)kCap) cand[slot] = pack(k, (uint32_t)e);
       }
-    });
+    };
+    if (vec) {
+      // a chunk can hold such an element only if its largest value reaches
+      // the value of t0.  A t0 at or below the key of -inf (its bit pattern
+      // would be a NaN) admits every element; -0 compares equal to +0.
+      constexpr int EPC = 16 / (int)sizeof(T);
+      const u32x4_t* p = (const u32x4_t*)row;
+      const int64_t chunks = V / EPC;
+      const float v0 = t0 <= Key<T>::of((T)-INFINITY) ? -INFINITY : value_of_key<T>(t0);
+#pragma unroll 4
+      for (int64_t c = tid; c < chunks; c += kTopkThreads) {
+        const u32x4_t v = p[c];
+        if (chunk_max(v, (T*)nullptr) >= v0) {
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) hold(Key<T>::of(chunk_elem(v, i, (T*)nullptr)), c * EPC + i);
+        }
+      }
+    } else {
+      for_each_key(row, V, vec, hold);
+    }
     __syncthreads();
     n_held = count;
     // every thread has read the count before the exact path may reset it
