@@ -12,11 +12,12 @@
 // Values are compared through an order-preserving unsigned key of their bits
 // (-0 is keyed as +0; NaN is outside the supported inputs):
 //  1. every thread takes the largest key of its strided share of the row;
-//  2. t0 = the lower edge of the histogram bin (top 12 key bits) in which,
+//  2. t0 = the lower edge of the histogram bin (top 13 key bits) in which,
 //     counting the maxima from the top, the K-th one falls; those K maxima
 //     are K distinct elements, so at least K keys are >= t0;
-//  3. the elements with key >= t0 are collected into LDS as (key, id) pairs
-//     (a second read of the row, mostly served by the caches);
+//  3. the elements with key >= t0 are collected into LDS as (key, id) pairs;
+//     each thread kept the largest value of every group of 8 of its chunks,
+//     so only the groups that reach t0 are read again (a few percent);
 //  4. ordered by (key descending, id ascending): each pair's place is the
 //     number of larger pairs (a bitonic sort when more pairs than threads).
 // When more than kCap elements reach t0 (many equal values near the top) or
@@ -34,7 +35,9 @@ namespace {
 
 constexpr int kTopkThreads = 512;
 constexpr int kCap = 4096;  // (key, id) pairs held in LDS (at least the largest K)
-constexpr int kHistBits = 12;
+constexpr int kGroup = 8;    // chunks per group whose maximum a thread keeps
+constexpr int kGroups = 16;  // groups per thread (bf16 rows up to 524,288, fp32 up to 262,144)
+constexpr int kHistBits = 13;
 constexpr int kHistBins = 1 << kHistBits;
 static_assert(kHistBins * 4 <= kCap * 8, "the histogram lives in the candidate store");
 static_assert(kHistBins % kTopkThreads == 0, "whole bins per thread");
@@ -213,6 +216,16 @@ __device__ inline void for_each_key(const T* row, int64_t V, bool vec, F&& fn) {
   }
 }
 
+// The input value of a held pair, rebuilt from its key; only a zero is read
+// back from the row, since -0 and +0 share one key and the value must keep
+// the input's sign.
+template <typename T>
+__device__ inline float value_out(uint64_t c, const T* row, uint32_t id) {
+  const uint32_t key = (uint32_t)(c >> 32);
+  if (key == Key<T>::of((T)0.f)) return (float)row[id];
+  return value_of_key<T>(key);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict__ x, int64_t V, int K,
                                                            int32_t* __restrict__ ids_out,
@@ -223,19 +236,40 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
   const int tid = threadIdx.x;
   const T* row = x + (int64_t)blockIdx.x * V;
   const bool vec = ((uintptr_t)row % 16 == 0) && ((V * (int64_t)sizeof(T)) % 16 == 0);
+  constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  const u32x4_t* p = (const u32x4_t*)row;
+  const uint32_t chunks = vec ? (uint32_t)(V / kEPC) : 0u;
+  // rows of at most kGroups x kGroup chunks per thread keep each group's maximum
+  const bool grouped = vec && chunks <= (uint32_t)(kGroups * kGroup * kTopkThreads);
+  float gmax[kGroups];
 
   bool exact = K > kTopkThreads;
   uint32_t n_held = 0;
   if (!exact) {
     // 1. largest key of this thread's share
     uint32_t mk = 0;  // 0 is below every element's key: a thread with no element
-    if (vec) {
-      const u32x4_t* p = (const u32x4_t*)row;
-      const int64_t chunks = V / (16 / (int64_t)sizeof(T));
+    if (grouped) {
+      float mv = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        float gm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          // loads clamped into the row and always issued, so that a group's
+          // loads are in flight together; chunks past the row are masked
+          const uint32_t c = (uint32_t)tid + (uint32_t)((g * kGroup + j) * kTopkThreads);
+          const float m = chunk_max(p[c < chunks ? c : chunks - 1], (T*)nullptr);
+          gm = fmaxf(gm, c < chunks ? m : -INFINITY);
+        }
+        gmax[g] = gm;
+        mv = fmaxf(mv, gm);
+      }
+      mk = (uint32_t)tid < chunks ? key_of_value<T>(mv) : 0u;
+    } else if (vec) {
       float mv = -INFINITY;
       bool any = false;
 #pragma unroll 4
-      for (int64_t c = tid; c < chunks; c += kTopkThreads) {
+      for (uint32_t c = tid; c < chunks; c += kTopkThreads) {
         mv = fmaxf(mv, chunk_max(p[c], (T*)nullptr));
         any = true;
       }
@@ -243,7 +277,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
     } else {
       for_each_key(row, V, vec, [&](uint32_t k, int64_t) { mk = max(mk, k); });
     }
-    // 2. t0 = the lower edge of the histogram bin (top 12 key bits) of the
+    // 2. t0 = the lower edge of the histogram bin (top 13 key bits) of the
     //    maxima where, counting from the top, K maxima are reached: at least
     //    K maxima, so K distinct elements, have key >= t0
     uint32_t* hist = (uint32_t*)cand;  // free until the candidates are collected
@@ -277,22 +311,32 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
         if (slot < (uint32_t)kCap) cand[slot] = pack(k, (uint32_t)e);
       }
     };
-    if (vec) {
-      // a chunk can hold such an element only if its largest value reaches
-      // the value of t0.  A t0 at or below the key of -inf (its bit pattern
-      // would be a NaN) admits every element; -0 compares equal to +0.
-      constexpr int EPC = 16 / (int)sizeof(T);
-      const u32x4_t* p = (const u32x4_t*)row;
-      const int64_t chunks = V / EPC;
-      const float v0 = t0 <= Key<T>::of((T)-INFINITY) ? -INFINITY : value_of_key<T>(t0);
-#pragma unroll 4
-      for (int64_t c = tid; c < chunks; c += kTopkThreads) {
-        const u32x4_t v = p[c];
-        if (chunk_max(v, (T*)nullptr) >= v0) {
+    // a chunk (or group) can hold such an element only if its largest value
+    // reaches the value of t0.  A t0 at or below the key of -inf (its bit
+    // pattern would be a NaN) admits every element; -0 compares equal to +0.
+    const float v0 = t0 <= Key<T>::of((T)-INFINITY) ? -INFINITY : value_of_key<T>(t0);
+    auto scan_chunk = [&](uint32_t c) {
+      const u32x4_t v = p[c];
+      if (chunk_max(v, (T*)nullptr) >= v0) {
 #pragma unroll
-          for (int i = 0; i < EPC; ++i) hold(Key<T>::of(chunk_elem(v, i, (T*)nullptr)), c * EPC + i);
+        for (int i = 0; i < kEPC; ++i)
+          hold(Key<T>::of(chunk_elem(v, i, (T*)nullptr)), (int64_t)c * kEPC + i);
+      }
+    };
+    if (grouped) {
+      // only the groups whose maximum (kept from step 1) reaches t0 are read again
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        if (gmax[g] >= v0) {
+          for (int j = 0; j < kGroup; ++j) {
+            const uint32_t c = (uint32_t)tid + (uint32_t)((g * kGroup + j) * kTopkThreads);
+            if (c < chunks) scan_chunk(c);
+          }
         }
       }
+    } else if (vec) {
+#pragma unroll 4
+      for (uint32_t c = tid; c < chunks; c += kTopkThreads) scan_chunk(c);
     } else {
       for_each_key(row, V, vec, hold);
     }
@@ -356,7 +400,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
       if (place < K) {
         const uint32_t id = unpack_id(c);
         io[place] = (int32_t)id;
-        vo[place] = (float)row[id];
+        vo[place] = value_out<T>(c, row, id);
       }
     }
     return;
@@ -369,7 +413,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
   for (int k = tid; k < K; k += kTopkThreads) {
     const uint32_t id = unpack_id(cand[k]);
     io[k] = (int32_t)id;
-    vo[k] = (float)row[id];
+    vo[k] = value_out<T>(cand[k], row, id);
   }
 }
 
