@@ -39,24 +39,35 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
+def traffic_path(kind):
+    return os.path.join(ROOT, "profiles", f"{kind}_gemm_hbm_traffic.json" if kind != "topk"
+                        else "topk_hbm_traffic.json")
+
+
 def traffic_from_profile(kernel_kind):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current GEMM sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_kind}_gemm_hbm_traffic.json")
+    was taken on the current sources of that kernel; else None."""
+    path = traffic_path(kernel_kind)
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             rec = json.load(f)
-        if rec.get("source_sha") != source_hash(GEMM_SOURCES):
+        if rec.get("source_sha") != source_hash(TRAFFIC_KINDS[kernel_kind][1]):
             return None
         return rec.get("bytes_per_launch")
     except (OSError, ValueError):
         return None
 
 
-KERNEL_SYMBOLS = {  # GEMM kind -> the EPI template argument its kernel name carries
-    "logits": "ELb1ELb1ELi0E", "dh": "ELb1ELb0ELi1E", "dw": "ELb0ELb0ELi2E"}
+TOPK_SOURCES = ["chunked_kl_loss_seq_amd/csrc/kernels_topk.hip"]
+# traffic record kind -> (substrings of the kernel name, sources the record is valid for)
+TRAFFIC_KINDS = {
+    "logits": (("gemm_kernel", "ELb1ELb1ELi0E"), GEMM_SOURCES),
+    "dh": (("gemm_kernel", "ELb1ELb0ELi1E"), GEMM_SOURCES),
+    "dw": (("gemm_kernel", "ELb0ELb0ELi2E"), GEMM_SOURCES),
+    "topk": (("topk_kernel", "DF16b"), TOPK_SOURCES),
+}
 
 
 def _counter_per_launch(path, name_filter, counter):
@@ -81,18 +92,21 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, commands
     cal_w, _ = _counter_per_launch(cal_write_csv, is_copy, "WRITE_SIZE")
     copy_kib = float(1 << 20)
     sf, sw = copy_kib / cal_f, copy_kib / cal_w
-    sha = source_hash(GEMM_SOURCES)
-    for kind, tag in KERNEL_SYMBOLS.items():
-        sel = lambda n, tag=tag: "gemm_kernel" in n and tag in n  # noqa: E731
-        f, nf = _counter_per_launch(fetch_csv, sel, "FETCH_SIZE")
-        w, nw = _counter_per_launch(write_csv, sel, "WRITE_SIZE")
-        rec = {"kernel": f"{kind} GEMM", "source_sha": sha, "launches": [nf, nw],
+    for kind, (tags, sources) in TRAFFIC_KINDS.items():
+        sel = lambda n, tags=tags: all(t in n for t in tags)  # noqa: E731
+        try:
+            f, nf = _counter_per_launch(fetch_csv, sel, "FETCH_SIZE")
+            w, nw = _counter_per_launch(write_csv, sel, "WRITE_SIZE")
+        except SystemExit:
+            continue  # that kernel did not run in these profiles
+        rec = {"kernel": kind if kind == "topk" else f"{kind} GEMM", "source_sha": source_hash(sources),
+               "launches": [nf, nw],
                "fetch_kib_per_launch_raw": f, "write_kib_per_launch_raw": w,
                "copy_calibration": {"bytes": 1 << 30, "fetch_kib": cal_f, "write_kib": cal_w,
                                     "fetch_scale": sf, "write_scale": sw},
                "fetch_bytes_per_launch": f * sf * 1024, "write_bytes_per_launch": w * sw * 1024,
                "bytes_per_launch": (f * sf + w * sw) * 1024, "commands": commands}
-        out = os.path.join(ROOT, "profiles", f"{kind}_gemm_hbm_traffic.json")
+        out = traffic_path(kind)
         with open(out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
@@ -179,7 +193,7 @@ def bench_topk(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "teacher-logits-gpt-oss-vocab", "rows": R, "V": V, "K": K, "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "top-K",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile("topk"), "kernel": "top-K",
                      "launch_avg_ms": round(launch_ms, 4)},
         "cpu_baseline": cpu,
     }
