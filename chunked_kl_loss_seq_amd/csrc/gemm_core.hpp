@@ -522,31 +522,53 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     // fp32 sum are what the row pass needs; the logits themselves are not kept.
     const int slice = (int)(mw / 128);
     T* pout = (T*)p.out;
+    // Ids past valid_m take no part in the max and the sum: selects on a
+    // 32-bit id for a tile that crosses valid_m, nothing for a full one (a
+    // branch per value would cost more than the exponentials).
+    const bool mfull = mw + WTM <= p.valid_m;
+    const int m0lane = (int)mw + h * 4;
+    const int vm = (int)(p.valid_m < (int64_t)0x7FFFFFFF ? p.valid_m : (int64_t)0x7FFFFFFF);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = nw + j * 32 + col;
-      float mx = -INFINITY;
+      float mx = -INFINITY, sum = 0.f;
+      if (mfull) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = mw + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          if (full || m < p.valid_m) mx = fmaxf(mx, acc[i][j][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float sum = 0.f;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = mw + i * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const float e = __expf(acc[i][j][r] - mx);
-          acc[i][j][r] = e;
-          if (full || m < p.valid_m) sum += e;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const float e = __expf(acc[i][j][r] - mx);
+            acc[i][j][r] = e;
+            sum += e;
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = m0lane + i * 32 + (r >> 2) * 8 + (r & 3) < vm;
+            mx = fmaxf(mx, ok ? acc[i][j][r] : -INFINITY);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = m0lane + i * 32 + (r >> 2) * 8 + (r & 3) < vm;
+            const float e = __expf(acc[i][j][r] - mx);
+            acc[i][j][r] = e;
+            sum += ok ? e : 0.f;
+          }
+      }
       sum += __shfl_xor(sum, 32);
       const bool nvalid = n < p.valid_n;
       if (h == 0 && nvalid && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, sum);
+      if constexpr (sizeof(T) == 2) continue;  // bf16: stored through LDS below
       if (nvalid) {
         // tile row of token n; the 4 values of (i, q) are consecutive ids
         T* prow = pout + (n >> 6) * p.ldo + (n & 63) * 64;
@@ -568,6 +590,45 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
               }
             }
           }
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+      // The wave's exp values are two whole 64 x 64 tiles of P (tokens nw ..
+      // nw + 63, vocabulary mw .. mw + 127), 8 KiB each and contiguous in
+      // memory, but a lane holds 4 consecutive ids of one token: stored
+      // directly, every wave store would touch 64 lines.  They go through this
+      // wave's 16 KiB of LDS (free once every wave has left the main loop) in
+      // the tiles' own order, 16-byte chunks of a token row XOR-swizzled by
+      // the row, and leave as 16 fully coalesced 1 KiB stores.
+      static_assert(WTM == 128 && WTN == 64 && NW * 16384 <= NS * STAGE, "one wave = two 64 x 64 tiles");
+      __syncthreads();
+      char* wl = smem + wave * 16384;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int t = 32 * j + col;  // token row within the tiles
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+            const bf16x4 v = {(__bf16)acc[i][j][4 * q], (__bf16)acc[i][j][4 * q + 1], (__bf16)acc[i][j][4 * q + 2],
+                              (__bf16)acc[i][j][4 * q + 3]};
+            const int chunk = 4 * (i & 1) + q;  // 16-byte chunk of the token row within tile i / 2
+            *(bf16x4*)(wl + (i >> 1) * 8192 + t * 128 + ((chunk ^ (t & 7)) << 4) + 8 * h) = v;
+          }
+      }
+      __syncthreads();
+      if (nw < p.valid_n) {
+        T* tile0 = pout + (nw >> 6) * p.ldo + (mw >> 6) * 4096;
+#pragma unroll
+        for (int sidx = 0; sidx < 16; ++sidx) {
+          const int idx = sidx * 64 + lane;
+          const int vb = idx >> 9, t = (idx >> 3) & 63, cc = idx & 7;
+          if (mw + 64 * vb < p.valid_m) {
+            const u32x4 v = *(const u32x4*)(wl + vb * 8192 + t * 128 + ((cc ^ (t & 7)) << 4));
+            *(u32x4*)(tile0 + vb * 4096 + t * 64 + cc * 8) = v;
+          }
+        }
       }
     }
   } else {
