@@ -116,21 +116,18 @@ def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=No
     """
     import torch
 
-    if not H.is_cuda:
-        raise ValueError("fwd_bwd needs GPU tensors")
+    _check_inputs(torch, H, W, ids, tlogit, "fwd_bwd", mask)
     N, d = H.shape
     V = W.shape[0]
     K = ids.shape[1]
-    for name, t in (("H", H), ("W", W), ("ids", ids), ("tlogit", tlogit)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if ids.dtype != torch.int32 or tlogit.dtype != torch.float32:
-        raise ValueError("ids must be int32 and tlogit float32")
-    if H.dtype != W.dtype or H.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("H and W must both be bfloat16 or both float32")
     if mask is not None:
         mask = mask.to(torch.uint8).contiguous()
     dev = H.device
+    _check_out(torch, out_loss, (), torch.float32, dev, "out_loss")
+    _check_out(torch, dH, (N, d), H.dtype, dev, "dH")
+    _check_out(torch, dW, (V, d), torch.float32, dev, "dW")
+    _check_out(torch, row_kl, (N,), torch.float32, dev, "row_kl")
+    _check_out(torch, row_lse, (N,), torch.float32, dev, "row_lse")
     if out_loss is None:
         out_loss = torch.empty((), dtype=torch.float32, device=dev)
     if dH is None:
@@ -151,28 +148,49 @@ def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=No
     return out_loss, dH, dW
 
 
-def _check_inputs(torch, H, W, ids, tlogit, what):
-    if not H.is_cuda:
+def _check_inputs(torch, H, W, ids, tlogit, what, mask=None, need_gpu=True):
+    """Dtypes, contiguity, one device and consistent shapes: the kernels index
+    every array by N, d, V and K, so a mismatch would read out of bounds."""
+    if need_gpu and not H.is_cuda:
         raise ValueError(f"{what} needs GPU tensors")
     for name, t in (("H", H), ("W", W), ("ids", ids), ("tlogit", tlogit)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if t.device != H.device:
+            raise ValueError(f"{name} must be on {H.device}")
     if ids.dtype != torch.int32 or tlogit.dtype != torch.float32:
         raise ValueError("ids must be int32 and tlogit float32")
     if H.dtype != W.dtype or H.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("H and W must both be bfloat16 or both float32")
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1]:
+        raise ValueError("H must be [N, d] and W [V, d]")
+    N = H.shape[0]
+    if ids.dim() != 2 or ids.shape[0] != N or tuple(tlogit.shape) != tuple(ids.shape):
+        raise ValueError("ids and tlogit must both be [N, K]")
+    if mask is not None and (tuple(mask.shape) != (N,) or mask.device != H.device):
+        raise ValueError(f"mask must be [N] on {H.device}")
     return DTYPE_BF16 if H.dtype == torch.bfloat16 else DTYPE_F32
+
+
+def _check_out(torch, t, shape, dtype, device, name):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
 
 
 def fwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, row_lse=None, row_kl=None):
     """Forward only: (loss 0-dim float32, row_lse float32 [N]); row_kl [N] filled when given."""
     import torch
 
-    dt = _check_inputs(torch, H, W, ids, tlogit, "fwd")
+    dt = _check_inputs(torch, H, W, ids, tlogit, "fwd", mask)
     N, d = H.shape
     V, K = W.shape[0], ids.shape[1]
     if mask is not None:
         mask = mask.to(torch.uint8).contiguous()
+    _check_out(torch, out_loss, (), torch.float32, H.device, "out_loss")
+    _check_out(torch, row_lse, (N,), torch.float32, H.device, "row_lse")
+    _check_out(torch, row_kl, (N,), torch.float32, H.device, "row_kl")
     if out_loss is None:
         out_loss = torch.empty((), dtype=torch.float32, device=H.device)
     if row_lse is None:
@@ -188,11 +206,16 @@ def bwd(H, W, ids, tlogit, row_lse, mask=None, grad_loss=None, chunk=0, dH=None,
     grad_loss x loss; grad_loss is a float32 device scalar tensor or None (1)."""
     import torch
 
-    dt = _check_inputs(torch, H, W, ids, tlogit, "bwd")
+    dt = _check_inputs(torch, H, W, ids, tlogit, "bwd", mask)
+    if row_lse is None:
+        raise ValueError("bwd needs the row_lse that fwd returned")
     N, d = H.shape
     V, K = W.shape[0], ids.shape[1]
     if mask is not None:
         mask = mask.to(torch.uint8).contiguous()
+    _check_out(torch, row_lse, (N,), torch.float32, H.device, "row_lse")
+    _check_out(torch, dH, (N, d), H.dtype, H.device, "dH")
+    _check_out(torch, dW, (V, d), torch.float32, H.device, "dW")
     if grad_loss is not None:
         grad_loss = grad_loss.to(device=H.device, dtype=torch.float32).contiguous()
     if dH is None:
@@ -217,6 +240,8 @@ def topk(logits, K, ids_out=None, vals_out=None):
         raise ValueError("logits must be bfloat16 or float32")
     N, V = logits.shape
     dt = DTYPE_BF16 if logits.dtype == torch.bfloat16 else DTYPE_F32
+    _check_out(torch, ids_out, (N, K), torch.int32, logits.device, "ids_out")
+    _check_out(torch, vals_out, (N, K), torch.float32, logits.device, "vals_out")
     if ids_out is None:
         ids_out = torch.empty((N, K), dtype=torch.int32, device=logits.device)
     if vals_out is None:
@@ -234,6 +259,10 @@ def debug_rows(Z, ids, tlogit, mask=None, scale=1.0, g_bf16=True):
     R, V = Z.shape
     K = ids.shape[1]
     dev = Z.device
+    if tuple(ids.shape) != (R, K) or tuple(tlogit.shape) != (R, K) or (mask is not None and tuple(mask.shape) != (R,)):
+        raise ValueError("ids and tlogit must be [R, K] and mask [R]")
+    if ids.dtype != torch.int32 or tlogit.dtype != torch.float32 or Z.dtype != torch.float32:
+        raise ValueError("Z and tlogit must be float32, ids int32")
     zg = torch.empty((R, K), dtype=torch.float32, device=dev)
     sid = torch.empty((R, K), dtype=torch.int32, device=dev)
     G = torch.empty((R, V), dtype=torch.bfloat16 if g_bf16 else torch.float32, device=dev)
