@@ -310,3 +310,32 @@ def test_gpt_oss_head_256k_sequence_workload_sampled():
     # one 262,144-token sequence: 32 chunks under the same 6 GiB workspace
     binding = _need_gpu()
     _sampled_full_size(binding, 6)
+
+
+# ------------------------------------------------------------------ limits of the supported shapes
+@pytest.mark.parametrize("shape", [
+    (1, 64, 500, 20, 0),        # one position
+    (40, 8, 3000, 2048, 0),     # the largest K, and the smallest d
+    (33, 16, 2048, 2048, 16),   # K = V at the largest K
+])
+def test_shape_limits(shape):
+    binding = _need_gpu()
+    N, d, V, K, chunk = shape
+    say(f"[case] shape limit N={N} d={d} V={V} K={K} chunk={chunk}")
+    inp = WL.small(N, d, V, K, dtype="f32", seed=N * 7 + K)
+    g = run_gpu(binding, inp, "f32", chunk=chunk, rows=True)
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], want_rows=True)
+    check(g, o, "f32", f"limit {shape}")
+
+
+def test_single_valid_position():
+    binding = _need_gpu()
+    say("[case] one valid position among 300")
+    inp = WL.small(300, 64, 2000, 30, dtype="bf16", seed=12)
+    inp["mask"][:] = 0
+    inp["mask"][137] = 1
+    g = run_gpu(binding, inp, "bf16", chunk=128)
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
+    check(g, o, "bf16", "one valid position")
+    rows = np.arange(300) != 137
+    assert np.all(g["dH"][rows] == 0)
