@@ -65,8 +65,8 @@ struct RowArgs {
   float* scat;          // [rows, K] exact gradient values at the cached ids
   const float* lse_in;  // [rows] log-normalisers saved by a forward pass, or null: merge the slice pairs
   const float* gscale;  // device scalar multiplying the gradient, or null for 1
-  float* kl_out;        // [rows] KL (0 for masked rows)
-  float* lse_out;       // [rows]
+  float* kl_out;        // [rows] KL (0 for masked rows), or null
+  float* lse_out;       // [rows] log-normalisers, or null
   float* zg_dbg;        // optional [rows, K]
   int32_t* sid_dbg;     // optional [rows, K]
 };
