@@ -61,6 +61,18 @@ __device__ inline int64_t elem_offset(const Operand& o, int64_t row, int64_t col
   return (row >> 6) * o.blk + (col >> 6) * 4096 + (row & 63) * 64 + (col & 63);
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp(z - mx) for the logits epilogue, nmx = -mx log2(e).  Values kept in
+// bf16 take 2^(z log2(e) + nmx), one fma and one exp instruction: its error,
+// |mx| log2(e) 2^-24 in the exponent, is far below bf16 rounding.  fp32
+// values take the subtraction first, exact for z near mx.
+template <typename T>
+__device__ inline float slice_exp(float z, float mx, float nmx) {
+  if constexpr (sizeof(T) == 2) return __builtin_amdgcn_exp2f(__builtin_fmaf(z, kLog2e, nmx));
+  return __expf(z - mx);
+}
+
 enum EpilogueKind : int {
   EPI_LOGITS = 0,  // per (n, 128-row slice of m): mx = max D, P[n][m] = exp(D[m][n] - mx), (mx, sum P)
   EPI_SLAB = 1,    // out[m][n] = D[m][n] (fp32), one slab per k-split
@@ -538,11 +550,12 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float nmx = -mx * kLog2e;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = __expf(acc[i][j][r] - mx);
+            const float e = slice_exp<T>(acc[i][j][r], mx, nmx);
             acc[i][j][r] = e;
             sum += e;
           }
@@ -555,12 +568,13 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
             mx = fmaxf(mx, ok ? acc[i][j][r] : -INFINITY);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float nmx = -mx * kLog2e;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const bool ok = m0lane + i * 32 + (r >> 2) * 8 + (r & 3) < vm;
-            const float e = __expf(acc[i][j][r] - mx);
+            const float e = slice_exp<T>(acc[i][j][r], mx, nmx);
             acc[i][j][r] = e;
             sum += ok ? e : 0.f;
           }
@@ -675,6 +689,20 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
         }
     }
   }
+}
+
+// ---------------------------------------------------------------- host side
+inline int cdiv64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// One launch over every tile of p; the grid is rounded up to a multiple of
+// the 8 XCDs so that each XCD gets the same share of the tile order.
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  const int total = p.tiles_m * p.tiles_n * p.splits;
+  const int grid = ((total + 7) / 8) * 8;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI, KB, NS>), dim3(grid), dim3(WM * WN * 64), 0, s,
+                     p);
+  return hipGetLastError();
 }
 
 }  // namespace ckl

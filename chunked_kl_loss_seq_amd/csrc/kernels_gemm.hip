@@ -1,25 +1,11 @@
-// Instantiations and launchers of the three contractions of the loss.
+// Launchers of the two gradient contractions (dH, dW), the tiled copy and the
+// split-K reduce.  The logits contraction has its own unit (kernels_logits.hip).
 #include "gemm_core.hpp"
 #include "launch.hpp"
 
 namespace ckl {
 
-namespace {
-
 constexpr int kGroupM = 4;
-
-inline int cdiv64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
-
-template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
-hipError_t run(GemmParams& p, hipStream_t s) {
-  const int total = p.tiles_m * p.tiles_n * p.splits;
-  const int grid = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI, KB, NS>), dim3(grid), dim3(WM * WN * 64), 0, s,
-                     p);
-  return hipGetLastError();
-}
-
-}  // namespace
 
 // bf16: 256-wide tiles along d (8 waves of 128 x 64), measured faster than
 // 192-wide ones even where 192 divides d and 256 does not; fp32 (wider
@@ -48,28 +34,6 @@ int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
   return best;
 }
 
-hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, hipStream_t s) {
-  GemmParams p{};
-  p.a = Operand{Wt, 0, V, d, tile_row_stride(d)};  // tiled: storage row = vocabulary id, column = d
-  p.b = Operand{Hc, d, rows, d, 0};
-  p.tiles_m = cdiv64(V, 256);
-  p.tiles_n = cdiv64(rows, 256);
-  const int bk = dt == DT_BF16 ? 64 : 32;
-  p.k_tiles = cdiv64(d, bk);
-  p.splits = 1;
-  p.k_tiles_per_split = p.k_tiles;
-  p.group_m = kGroupM;
-  p.out = P;
-  p.ldo = pblk;
-  p.valid_m = V;
-  p.valid_n = rows;
-  p.part = part;
-  p.n_slices = n_slices;
-  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
-  return run<float, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
-}
-
 hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,
                      float* slab, int splits, hipStream_t s) {
   const int bn = d_tile(dt, d);
@@ -89,9 +53,9 @@ hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int6
   p.valid_m = rows;
   p.valid_n = d;
   if (p.splits != splits) return hipErrorInvalidValue;
-  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, true, false, EPI_SLAB, 128, 2>(p, s);
-  if (bn == 192) return run<float, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
-  return run<float, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
+  if (dt == DT_BF16) return launch_gemm<__bf16, 256, 256, 2, 4, true, false, EPI_SLAB, 128, 2>(p, s);
+  if (bn == 192) return launch_gemm<float, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
+  return launch_gemm<float, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
 }
 
 hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int64_t V, int64_t d, int64_t rows,
@@ -112,9 +76,9 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int6
   p.valid_m = V;
   p.valid_n = d;
   p.beta = beta;
-  if (dt == DT_BF16) return run<__bf16, 256, 256, 2, 4, false, false, EPI_ACCUM, 128, 2>(p, s);
-  if (bn == 192) return run<float, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
-  return run<float, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
+  if (dt == DT_BF16) return launch_gemm<__bf16, 256, 256, 2, 4, false, false, EPI_ACCUM, 128, 2>(p, s);
+  if (bn == 192) return launch_gemm<float, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
+  return launch_gemm<float, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
 }
 
 // ---------------------------------------------------------------- tiled copy

@@ -1,0 +1,32 @@
+// Launcher of the logits contraction with its fused exp epilogue.  It is a
+// unit of its own so that it can be compiled with the scheduler that favours
+// latency over register pressure: the fragment reads of a sub-step are then
+// issued a whole sub-step of MFMAs ahead of their use.
+#include "gemm_core.hpp"
+#include "launch.hpp"
+
+namespace ckl {
+
+hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
+                         int64_t pblk, float2* part, int n_slices, hipStream_t s) {
+  GemmParams p{};
+  p.a = Operand{Wt, 0, V, d, tile_row_stride(d)};  // tiled: storage row = vocabulary id, column = d
+  p.b = Operand{Hc, d, rows, d, 0};
+  p.tiles_m = cdiv64(V, 256);
+  p.tiles_n = cdiv64(rows, 256);
+  const int bk = dt == DT_BF16 ? 64 : 32;
+  p.k_tiles = cdiv64(d, bk);
+  p.splits = 1;
+  p.k_tiles_per_split = p.k_tiles;
+  p.group_m = 4;
+  p.out = P;
+  p.ldo = pblk;
+  p.valid_m = V;
+  p.valid_n = rows;
+  p.part = part;
+  p.n_slices = n_slices;
+  if (dt == DT_BF16) return launch_gemm<__bf16, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
+  return launch_gemm<float, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
+}
+
+}  // namespace ckl
