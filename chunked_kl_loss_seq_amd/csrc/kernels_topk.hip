@@ -16,8 +16,9 @@
 //     counting the maxima from the top, the K-th one falls; those K maxima
 //     are K distinct elements, so at least K keys are >= t0;
 //  3. the elements with key >= t0 are collected into LDS as (key, id) pairs;
-//     each thread kept the largest value of every group of 8 of its chunks,
-//     so only the groups that reach t0 are read again (a few percent);
+//     each thread kept the largest value of each of its 16-byte chunks (bf16
+//     rows) or of every group of 8 of them (fp32 rows), so only the chunks or
+//     groups that reach t0 are read again (a few percent of the row);
 //  4. ordered by (key descending, id ascending): each pair's place is the
 //     number of larger pairs (a bitonic sort when more pairs than threads).
 // When more than kCap elements reach t0 (many equal values near the top) or
@@ -35,8 +36,6 @@ namespace {
 
 constexpr int kTopkThreads = 512;
 constexpr int kCap = 4096;  // (key, id) pairs held in LDS (at least the largest K)
-constexpr int kGroup = 8;    // chunks per group whose maximum a thread keeps
-constexpr int kGroups = 16;  // groups per thread (bf16 rows up to 524,288, fp32 up to 262,144)
 constexpr int kHistBits = 13;
 constexpr int kHistBins = 1 << kHistBits;
 static_assert(kHistBins * 4 <= kCap * 8, "the histogram lives in the candidate store");
@@ -106,6 +105,38 @@ __device__ inline uint32_t key_of_value(float v) {
   else
     return Key<float>::of(v);
 }
+
+// Per-thread maxima kept from the first pass so that the second pass reads
+// again only what can reach the threshold.  bf16 rows keep the maximum of
+// every chunk (exact in bf16, two per register; a re-read then touches one
+// 16-byte chunk instead of eight scattered ones); fp32 rows keep the maximum
+// of every group of 8 chunks.  Rows with more chunks per thread than kept
+// here are scanned again whole.
+template <typename T>
+struct GroupMax;
+template <>
+struct GroupMax<__bf16> {
+  static constexpr int kGroup = 1;    // chunks per group
+  static constexpr int kGroups = 64;  // groups per thread: rows up to 262,144 bf16
+  uint32_t w[kGroups / 2];
+  // m holds a bf16 value exactly (or -inf)
+  __device__ inline void set(int g, float m) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, m) >> 16;
+    w[g >> 1] = (g & 1) ? ((w[g >> 1] & 0xFFFFu) | (b << 16)) : b;
+  }
+  __device__ inline float get(int g) const {
+    const uint32_t b = (g & 1) ? (w[g >> 1] & 0xFFFF0000u) : (w[g >> 1] << 16);
+    return __builtin_bit_cast(float, b);
+  }
+};
+template <>
+struct GroupMax<float> {
+  static constexpr int kGroup = 8;
+  static constexpr int kGroups = 16;  // rows up to 262,144 fp32
+  float w[kGroups];
+  __device__ inline void set(int g, float m) { w[g] = m; }
+  __device__ inline float get(int g) const { return w[g]; }
+};
 
 // The value whose key is t, for t above the key of -inf (below it the bit
 // patterns are NaNs): the keys invert back to bit patterns.
@@ -239,9 +270,11 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
   constexpr int kEPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   const u32x4_t* p = (const u32x4_t*)row;
   const uint32_t chunks = vec ? (uint32_t)(V / kEPC) : 0u;
+  typedef GroupMax<T> GM;
+  constexpr int kGroup = GM::kGroup, kGroups = GM::kGroups;
   // rows of at most kGroups x kGroup chunks per thread keep each group's maximum
   const bool grouped = vec && chunks <= (uint32_t)(kGroups * kGroup * kTopkThreads);
-  float gmax[kGroups];
+  GM gmax;
 
   bool exact = K > kTopkThreads;
   uint32_t n_held = 0;
@@ -261,7 +294,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
           const float m = chunk_max(p[c < chunks ? c : chunks - 1], (T*)nullptr);
           gm = fmaxf(gm, c < chunks ? m : -INFINITY);
         }
-        gmax[g] = gm;
+        gmax.set(g, gm);
         mv = fmaxf(mv, gm);
       }
       mk = (uint32_t)tid < chunks ? key_of_value<T>(mv) : 0u;
@@ -324,14 +357,19 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const T* __restrict_
       }
     };
     if (grouped) {
-      // only the groups whose maximum (kept from step 1) reaches t0 are read again
+      // only the groups whose maximum (kept from step 1) reaches t0 are read
+      // again: a bit mask of them first (register indices stay static), then
+      // one pass over its set bits
+      static_assert(kGroups <= 64, "one bit per group");
+      uint64_t todo = 0;
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        if (gmax[g] >= v0) {
-          for (int j = 0; j < kGroup; ++j) {
-            const uint32_t c = (uint32_t)tid + (uint32_t)((g * kGroup + j) * kTopkThreads);
-            if (c < chunks) scan_chunk(c);
-          }
+      for (int g = 0; g < kGroups; ++g) todo |= (uint64_t)(gmax.get(g) >= v0) << g;
+      while (todo) {
+        const int g = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        for (int j = 0; j < kGroup; ++j) {
+          const uint32_t c = (uint32_t)tid + (uint32_t)((g * kGroup + j) * kTopkThreads);
+          if (c < chunks) scan_chunk(c);
         }
       }
     } else if (vec) {
