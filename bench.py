@@ -24,7 +24,11 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
-GEMM_SOURCES = ["chunked_kl_loss_seq_amd/csrc/gemm_core.hpp", "chunked_kl_loss_seq_amd/csrc/kernels_gemm.hip"]
+# sources (and the build script, which holds the compiler flags) a traffic record is valid for
+BUILD = "chunked_kl_loss_seq_amd/build.py"
+GEMM_SOURCES = ["chunked_kl_loss_seq_amd/csrc/gemm_core.hpp", "chunked_kl_loss_seq_amd/csrc/kernels_gemm.hip", BUILD]
+LOGITS_SOURCES = ["chunked_kl_loss_seq_amd/csrc/gemm_core.hpp", "chunked_kl_loss_seq_amd/csrc/kernels_logits.hip",
+                  BUILD]
 
 
 def log(*a):
@@ -60,10 +64,10 @@ def traffic_from_profile(kernel_kind):
         return None
 
 
-TOPK_SOURCES = ["chunked_kl_loss_seq_amd/csrc/kernels_topk.hip"]
+TOPK_SOURCES = ["chunked_kl_loss_seq_amd/csrc/kernels_topk.hip", BUILD]
 # traffic record kind -> (substrings of the kernel name, sources the record is valid for)
 TRAFFIC_KINDS = {
-    "logits": (("gemm_kernel", "ELb1ELb1ELi0E"), GEMM_SOURCES),
+    "logits": (("gemm_kernel", "ELb1ELb1ELi0E"), LOGITS_SOURCES),
     "dh": (("gemm_kernel", "ELb1ELb0ELi1E"), GEMM_SOURCES),
     "dw": (("gemm_kernel", "ELb0ELb0ELi2E"), GEMM_SOURCES),
     "topk": (("topk_kernel", "DF16b"), TOPK_SOURCES),
