@@ -109,3 +109,14 @@ def test_full_vocabulary_rows():
     assert np.all(np.diff(s, axis=1) > 0) and s.min() >= 0 and s.max() < V
     kth = vals[:, -1:]
     assert np.all((x > kth).sum(axis=1) < K) and np.all((x >= kth).sum(axis=1) >= K)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 262144), ("bf16", 262152), ("bf16", 300000), ("f32", 262144),
+                                     ("f32", 262148)])
+def test_long_rows_around_the_kept_maxima_limit(dtype, V):
+    # the first pass keeps, per thread, the maximum of every 16-byte chunk of a
+    # bf16 row (up to 262,144 elements) or of every 8 chunks of an fp32 row (up
+    # to 262,144 elements); longer rows are scanned again whole
+    binding = _need_gpu()
+    x = WL.teacher_logits(6, V, seed=V, bf16=dtype == "bf16")
+    check_exact(binding, x, 100, dtype, f"{dtype} V={V}")
