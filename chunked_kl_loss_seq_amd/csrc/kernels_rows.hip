@@ -210,8 +210,9 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
       const int id = iv[q];
       const float ms = prow[id >> 7].x;
       const float pv = to_f(P[tile_off(r, id, a.pblk)]);
-      // z = m + log p; a p that underflowed to zero (z more than ~103 below
-      // its slice max) is read as the smallest positive float
+      // z = m + log p; a p that underflowed to zero (z more than about 92
+      // below its slice max in bf16, 103 in fp32) is read as the smallest
+      // positive float
       const float zg = ms + logf(fmaxf(pv, 1.4e-45f));
       const float lpt = tv[q] - lse_t;
       const float pt = __expf(lpt);
