@@ -339,3 +339,36 @@ def test_single_valid_position():
     check(g, o, "bf16", "one valid position")
     rows = np.arange(300) != 137
     assert np.all(g["dH"][rows] == 0)
+
+
+# ------------------------------------------------------------------ seeded random sweep
+def _sweep_cases(n=14, seed=20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 3 == 0 else "bf16"
+        K = int(rng.integers(1, 300))
+        V = int(rng.integers(max(2 * K, 64), 7000))
+        d = 8 * int(rng.integers(1, 49))
+        N = int(rng.integers(1, 900))
+        chunk = [0, N, 64 * int(rng.integers(1, 9))][int(rng.integers(0, 3))]
+        kinds = ["uniform", "overlap50"] + (["zipf"] if K <= V // 4 else [])
+        ids = kinds[int(rng.integers(0, len(kinds)))]
+        mask = ["none", "random5"][int(rng.integers(0, 2))]
+        cases.append((dtype, N, d, V, K, chunk, ids, mask))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "-".join(str(x) for x in c))
+def test_seeded_random_shapes(case):
+    # shapes, chunk sizes, id distributions and masks drawn from a fixed seed:
+    # ragged in every dimension, d from 8 to 384, K from 1 to 299
+    binding = _need_gpu()
+    dtype, N, d, V, K, chunk, ids, mask = case
+    say(f"[case] sweep {case}")
+    inp = WL.small(N, d, V, K, dtype=dtype, ids=ids, mask=mask, seed=N * 7 + V)
+    g = run_gpu(binding, inp, dtype, chunk=chunk)
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
+    check(g, o, dtype, f"sweep {case}")
+    valid = inp["mask"] == 1
+    assert np.all(g["dH"][~valid] == 0)
