@@ -112,7 +112,8 @@ def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=No
     tlogit float32 [N,K]; mask uint8/bool [N] or None.  Returns
     (loss 0-dim float32, dH like H, dW float32 [V,d]), all enqueued on the
     current stream.  ``row_kl`` / ``row_lse`` (float32 [N] tensors) receive
-    the per-position KL and student logsumexp when given.
+    the per-position KL and student logsumexp when given (both 0 for masked
+    positions).
     """
     import torch
 
@@ -180,7 +181,8 @@ def _check_out(torch, t, shape, dtype, device, name):
 
 
 def fwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, row_lse=None, row_kl=None):
-    """Forward only: (loss 0-dim float32, row_lse float32 [N]); row_kl [N] filled when given."""
+    """Forward only: (loss 0-dim float32, row_lse float32 [N], 0 for masked positions); row_kl [N]
+    filled when given."""
     import torch
 
     dt = _check_inputs(torch, H, W, ids, tlogit, "fwd", mask)

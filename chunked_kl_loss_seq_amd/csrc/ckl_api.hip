@@ -34,7 +34,7 @@ struct Layout {
   int n_slices = 0;     // (max, sum exp) pairs per row
   int splits = 0;       // k-splits of the dH contraction
   uint64_t w_off = 0, p_off = 0, part_off = 0, scat_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0,
-           total = 0;
+           hc_off = 0, idc_off = 0, tlc_off = 0, vidx_off = 0, pos_off = 0, total = 0;
 };
 
 Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t esz) {
@@ -61,6 +61,18 @@ Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_
   off += align256((uint64_t)N * 4);
   L.scal_off = off;
   off += 256;
+  // compacted chunk (calls with a mask): valid rows of H, ids and teacher
+  // logits, and the index maps
+  L.hc_off = off;
+  off += align256((uint64_t)C * d * esz);
+  L.idc_off = off;
+  off += align256((uint64_t)C * K * 4);
+  L.tlc_off = off;
+  off += align256((uint64_t)C * K * 4);
+  L.vidx_off = off;
+  off += align256((uint64_t)C * 4);
+  L.pos_off = off;
+  off += align256((uint64_t)C * 4);
   L.total = off;
   return L;
 }
@@ -233,6 +245,14 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   float* kl = row_kl ? row_kl : (float*)(base + L.kl_off);
   float* lse = row_lse ? row_lse : (float*)(base + L.lse_off);
   void* scal = base + L.scal_off;
+  // with a mask, every chunk is compacted to its valid rows; their count lives
+  // in the scalar block, after the valid count and scale
+  int* live = mask ? (int*)((char*)scal + 64) : nullptr;
+  void* Hcc = base + L.hc_off;
+  int32_t* idc = (int32_t*)(base + L.idc_off);
+  float* tlc = (float*)(base + L.tlc_off);
+  int* vidx = (int*)(base + L.vidx_off);
+  int* pos = (int*)(base + L.pos_off);
 
   {
     Timed t(T_OTHER, stream);
@@ -242,9 +262,20 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   for (int64_t r0 = 0; r0 < N; r0 += L.C) {
     const int64_t rows = (N - r0) < L.C ? (N - r0) : L.C;
     const void* Hc = (const char*)H + (size_t)r0 * d * esz;
+    const int32_t* ids_c = ids + r0 * K;
+    const float* tl_c = tlogit + r0 * K;
+    float* lse_c = pass == PASS_BWD ? nullptr : lse + r0;
+    if (live) {
+      Timed t(T_OTHER, stream);
+      CKL_TRY(launch_compact(dt, mask + r0, rows, L.C, Hc, d, ids_c, tl_c, (int)K, vidx, pos, live, kl + r0, lse_c,
+                             Hcc, idc, tlc, stream));
+      Hc = Hcc;
+      ids_c = idc;
+      tl_c = tlc;
+    }
     {
       Timed t(T_LOGITS, stream);
-      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, stream));
+      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, live, stream));
     }
     {
       RowArgs a{};
@@ -252,18 +283,20 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       a.pblk = L.pblk;
       a.part = part;
       a.n_slices = L.n_slices;
-      a.ids = ids + r0 * K;
-      a.tlogit = tlogit + r0 * K;
-      a.mask = mask ? mask + r0 : nullptr;
+      a.ids = ids_c;
+      a.tlogit = tl_c;
+      a.mask = nullptr;  // without a mask every row counts; with one, the compacted rows all do
       a.scal = scal;
       a.V = V;
       a.K = (int)K;
       a.rows = rows;
       a.scat = scat;
       a.kl_out = kl + r0;
-      a.lse_out = pass == PASS_BWD ? nullptr : lse + r0;
+      a.lse_out = lse_c;
       a.lse_in = pass == PASS_BWD ? lse_in + r0 : nullptr;
       a.gscale = pass == PASS_BWD ? gscale : nullptr;
+      a.live = live;
+      a.vidx = live ? vidx : nullptr;
       Timed t(T_ROWS, stream);
       CKL_TRY(launch_row_stats(dt, a, stream));
       if (want_grad) {
@@ -277,15 +310,16 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
     if (splits > cap) splits = (int)cap;
     {
       Timed t(T_DH, stream);
-      CKL_TRY(launch_dh(dt, P, L.pblk, Wt, V, d, rows, slab, splits, stream));
+      CKL_TRY(launch_dh(dt, P, L.pblk, Wt, V, d, rows, slab, splits, live, stream));
     }
     {
       Timed t(T_DHRED, stream);
-      CKL_TRY(launch_dh_reduce(dt, slab, splits, rows, d, (char*)dH + (size_t)r0 * d * esz, stream));
+      CKL_TRY(launch_dh_reduce(dt, slab, splits, rows, d, live ? pos : nullptr, (char*)dH + (size_t)r0 * d * esz,
+                               stream));
     }
     {
       Timed t(T_DW, stream);
-      CKL_TRY(launch_dw(dt, P, L.pblk, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, stream));
+      CKL_TRY(launch_dw(dt, P, L.pblk, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, live, stream));
     }
   }
   if (want_loss) {

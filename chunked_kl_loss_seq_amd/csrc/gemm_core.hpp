@@ -93,6 +93,10 @@ struct GemmParams {
   float2* part;          // EPI_LOGITS: partial (max, sum exp) per [n][slice]
   int n_slices;          // EPI_LOGITS: slices per row of part
   int beta;              // EPI_ACCUM
+  // Device int or null: the chunk's rows (tokens) at and after *live are all
+  // masked.  Logits tiles of those rows return at once, dH tiles of them
+  // write zeros without a k-loop, and dW (k = rows) stops its k-loop there.
+  const int* live;
 };
 
 // ---------------------------------------------------------------- LDS layouts
@@ -410,7 +414,17 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   const int wm = wave % WM, wn = wave / WM;
   const int64_t m0 = (int64_t)tc.tm * BM, n0 = (int64_t)tc.tn * BN;
   const int kt_begin = tc.split * p.k_tiles_per_split;
-  const int kt_end = min(p.k_tiles, kt_begin + p.k_tiles_per_split);
+  int kt_end = min(p.k_tiles, kt_begin + p.k_tiles_per_split);
+  if (p.live != nullptr) {
+    const int lv = __builtin_amdgcn_readfirstlane(*p.live);
+    if constexpr (EPI == EPI_LOGITS) {
+      if (n0 >= lv) return;  // whole workgroup: no barrier reached yet
+    } else if constexpr (EPI == EPI_SLAB) {
+      if (m0 >= lv) kt_end = kt_begin;  // the epilogue writes this tile's zeros
+    } else {
+      kt_end = min(kt_end, (lv + BK - 1) / BK);  // rows are the k dimension
+    }
+  }
 
   f32x16 acc[FM][FN];
 #pragma unroll

@@ -35,10 +35,11 @@ int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
 }
 
 hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,
-                     float* slab, int splits, hipStream_t s) {
+                     float* slab, int splits, const int* live, hipStream_t s) {
   const int bn = d_tile(dt, d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
+  p.live = live;
   p.a = Operand{G, 0, rows, V, gblk};  // tiled: storage row = token, column = vocabulary id
   p.b = Operand{Wt, 0, d, V, tile_row_stride(d)};  // tiled: storage row = vocabulary id (k), column = d (n)
   p.tiles_m = cdiv64(rows, 256);
@@ -59,10 +60,11 @@ hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int6
 }
 
 hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int64_t V, int64_t d, int64_t rows,
-                     float* dW, int beta, hipStream_t s) {
+                     float* dW, int beta, const int* live, hipStream_t s) {
   const int bn = d_tile(dt, d);
   const int bk = dt == DT_BF16 ? 64 : 32;
   GemmParams p{};
+  p.live = live;
   p.a = Operand{G, 0, V, rows, gblk};  // tiled: storage row = token (k), column = vocabulary id (m)
   p.b = Operand{Hc, d, d, rows, 0};
   p.tiles_m = cdiv64(V, 256);
@@ -107,13 +109,27 @@ hipError_t launch_tile_copy(Dtype dt, const void* src, int64_t rows, int64_t col
 }
 
 // ---------------------------------------------------------------- split-K reduce
+// Thread: 4 consecutive dH elements of one row (d % 8 == 0).  With pos, the
+// output row j reads slab row pos[j] (a compacted chunk) or writes zeros.
 template <typename TO>
 __global__ void __launch_bounds__(256) dh_reduce_kernel(const float* __restrict__ slab, int splits, int64_t count,
+                                                       int64_t d, const int* __restrict__ pos,
                                                        TO* __restrict__ out) {
   const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i4 >= count) return;
-  f32x4 acc = *(const f32x4*)(slab + i4);
-  for (int s = 1; s < splits; ++s) acc += *(const f32x4*)(slab + (int64_t)s * count + i4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int64_t src = i4;
+  bool live = true;
+  if (pos != nullptr) {
+    const int64_t j = i4 / d;
+    const int p = pos[j];
+    live = p >= 0;
+    src = (int64_t)p * d + (i4 - j * d);
+  }
+  if (live) {
+    acc = *(const f32x4*)(slab + src);
+    for (int s = 1; s < splits; ++s) acc += *(const f32x4*)(slab + (int64_t)s * count + src);
+  }
   if constexpr (sizeof(TO) == 4) {
     *(f32x4*)((float*)out + i4) = acc;
   } else {
@@ -123,16 +139,16 @@ __global__ void __launch_bounds__(256) dh_reduce_kernel(const float* __restrict_
   }
 }
 
-hipError_t launch_dh_reduce(Dtype dt, const float* slab, int splits, int64_t rows, int64_t d, void* dH,
-                            hipStream_t s) {
+hipError_t launch_dh_reduce(Dtype dt, const float* slab, int splits, int64_t rows, int64_t d, const int* pos,
+                            void* dH, hipStream_t s) {
   const int64_t count = rows * d;  // d % 8 == 0, so count % 4 == 0
   const int64_t blocks = (count / 4 + 255) / 256;
   if (dt == DT_BF16)
-    hipLaunchKernelGGL(dh_reduce_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, slab, splits, count,
-                       (__bf16*)dH);
+    hipLaunchKernelGGL(dh_reduce_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s, slab, splits, count, d,
+                       pos, (__bf16*)dH);
   else
-    hipLaunchKernelGGL(dh_reduce_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, slab, splits, count,
-                       (float*)dH);
+    hipLaunchKernelGGL(dh_reduce_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, slab, splits, count, d,
+                       pos, (float*)dH);
   return hipGetLastError();
 }
 

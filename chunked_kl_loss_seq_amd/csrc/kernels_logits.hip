@@ -8,8 +8,9 @@
 namespace ckl {
 
 hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, hipStream_t s) {
+                         int64_t pblk, float2* part, int n_slices, const int* live, hipStream_t s) {
   GemmParams p{};
+  p.live = live;
   p.a = Operand{Wt, 0, V, d, tile_row_stride(d)};  // tiled: storage row = vocabulary id, column = d
   p.b = Operand{Hc, d, rows, d, 0};
   p.tiles_m = cdiv64(V, 256);

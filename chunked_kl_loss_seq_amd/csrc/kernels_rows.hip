@@ -24,6 +24,11 @@
 //     gradient value at each cached id, f_rs p - w_r p_T;
 //  2. dense: G = f_rs p over every tile, in place (same element, same type);
 //  3. scatter: G at the cached ids <- the exact values of step 1.
+// With a mask, each chunk is first compacted: its valid rows (H, cached ids
+// and logits) are gathered, in order, to the front of chunk buffers, and every
+// kernel of the chunk runs on those `live` rows only.  Masked rows get no
+// logits and no GEMM work; they report KL 0 and log-normaliser 0, and their
+// dH rows are written as zeros.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -149,6 +154,77 @@ __global__ void __launch_bounds__(1024) mask_count_kernel(const uint8_t* __restr
   }
 }
 
+// Compaction of one chunk of `rows` positions (mask, row outputs and the
+// index arrays relative to the chunk): vidx[i] = the chunk row of the i-th
+// valid position, pos[j] = the compact index of chunk row j or -1, *live =
+// the valid count.  Masked rows' KL and log-normaliser are written as 0 here.
+// One workgroup; thread t takes a contiguous run of rows.
+__global__ void __launch_bounds__(1024) compact_scan_kernel(const uint8_t* __restrict__ mask, int64_t rows,
+                                                           int* __restrict__ vidx, int* __restrict__ pos,
+                                                           int* __restrict__ live, float* __restrict__ kl_out,
+                                                           float* __restrict__ lse_out) {
+  __shared__ int red[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t per = (rows + 1023) / 1024;
+  const int64_t j0 = min(rows, tid * per), j1 = min(rows, j0 + per);
+  int n = 0;
+  for (int64_t j = j0; j < j1; ++j) n += mask[j] != 0;
+  // exclusive prefix of n over threads: within the wave, then over waves
+  int x = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) red[w] = x;
+  __syncthreads();
+  int before = x - n;
+  for (int i = 0; i < w; ++i) before += red[i];
+  for (int64_t j = j0; j < j1; ++j) {
+    if (mask[j] != 0) {
+      vidx[before] = (int)j;
+      pos[j] = before++;
+    } else {
+      pos[j] = -1;
+      kl_out[j] = 0.f;
+      if (lse_out) lse_out[j] = 0.f;
+    }
+  }
+  if (tid == 1023) *live = before;
+}
+
+// Gather of the live rows: Hc[i] = H[vidx[i]], ids and teacher logits alike,
+// for i < *live; rows [*live, next multiple of 256) of Hc are zeroed, since
+// the logits and dW contractions read whole 256-row tiles and 64-row k-steps
+// (their gradient rows are zero, and zero times a stale NaN would not be).
+// One workgroup per row; d % 8 == 0.
+template <typename T>
+__global__ void __launch_bounds__(256) compact_gather_kernel(const int* __restrict__ vidx, const int* __restrict__ live,
+                                                            int64_t rows_alloc, const T* __restrict__ H, int64_t d,
+                                                            const int32_t* __restrict__ ids,
+                                                            const float* __restrict__ tlogit, int K,
+                                                            T* __restrict__ Hc, int32_t* __restrict__ ids_c,
+                                                            float* __restrict__ tl_c) {
+  const int64_t i = blockIdx.x;
+  const int n = *live;
+  const int64_t zero_end = min(rows_alloc, ((int64_t)n + 255) / 256 * 256);
+  if (i >= zero_end) return;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  T* dst = Hc + i * d;
+  if (i < n) {
+    const int64_t src = vidx[i];
+    const T* s = H + src * d;
+    for (int64_t c = threadIdx.x; c < d / EPC; c += 256) ((u32x4*)dst)[c] = ((const u32x4*)s)[c];
+    for (int k = threadIdx.x; k < K; k += 256) {
+      ids_c[i * K + k] = ids[src * K + k];
+      tl_c[i * K + k] = tlogit[src * K + k];
+    }
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t c = threadIdx.x; c < d / EPC; c += 256) ((u32x4*)dst)[c] = z;
+  }
+}
+
 // ------------------------------------------------------------------ 1. row statistics
 // One workgroup per token row.
 template <typename T>
@@ -157,6 +233,10 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
   __shared__ float red[2 * (NT / 64)];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
+  if (a.live != nullptr && r >= *a.live) return;  // past the compacted rows
+  // row outputs (and a saved log-normaliser) belong to the chunk row this
+  // compacted row came from
+  const int64_t ro = a.vidx != nullptr ? a.vidx[r] : r;
   const Scalars* sc = (const Scalars*)a.scal;
   const float scale = sc ? sc->scale : a.scale_value;
   const bool valid = a.mask == nullptr || a.mask[r] != 0;
@@ -168,7 +248,7 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
   // GEMM and the merge order do not depend on the chunking)
   float lse;
   if (a.lse_in) {
-    lse = a.lse_in[r];
+    lse = a.lse_in[ro];
   } else {
     float m = -INFINITY, s = 0.f;
     for (int p = tid; p < a.n_slices; p += NT) {
@@ -233,8 +313,8 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
     prow[p].y = valid ? w * __expf(q.x - lse) : 0.f;
   }
   if (tid == 0) {
-    if (a.kl_out) a.kl_out[r] = valid ? kl : 0.f;
-    if (a.lse_out) a.lse_out[r] = lse;
+    if (a.kl_out) a.kl_out[ro] = valid ? kl : 0.f;
+    if (a.lse_out) a.lse_out[ro] = valid ? lse : 0.f;
   }
 }
 
@@ -248,9 +328,10 @@ __global__ void __launch_bounds__(256) dense_kernel(RowArgs a) {
   const int64_t r = tb * 64 + (tid >> 2);
   const int64_t v0 = vb * 64 + (tid & 3) * 16;
   T* g = (T*)a.P + tile_off(r, v0, a.pblk);
-  // rows past the chunk hold no exp values (possibly not even numbers): they
-  // are written as zeros without being read into the product
-  const bool row_ok = r < a.rows;
+  // rows past the chunk, or past its compacted rows, hold no exp values
+  // (possibly not even numbers): they are written as zeros without being read
+  // into the product
+  const bool row_ok = r < a.rows && (a.live == nullptr || r < *a.live);
   float f = 0.f;
   if (row_ok && v0 < a.V) f = a.part[r * a.n_slices + (v0 >> 7)].y;
   if constexpr (sizeof(T) == 2) {
@@ -281,6 +362,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(RowArgs a) {
   if (i >= a.rows * a.K) return;
   const int64_t r = i / a.K;
   if (a.mask != nullptr && a.mask[r] == 0) return;
+  if (a.live != nullptr && r >= *a.live) return;  // past the compacted rows: no ids
   const int id = a.ids[i];
   ((T*)a.P)[tile_off(r, id, a.pblk)] = (T)a.scat[i];
 }
@@ -339,6 +421,21 @@ __global__ void __launch_bounds__(1024) finalize_kernel(const float* __restrict_
 }
 
 }  // namespace
+
+hipError_t launch_compact(Dtype dt, const uint8_t* mask, int64_t rows, int64_t rows_alloc, const void* H,
+                          int64_t d, const int32_t* ids, const float* tlogit, int K, int* vidx, int* pos,
+                          int* live, float* kl_out, float* lse_out, void* Hc, int32_t* ids_c, float* tl_c,
+                          hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, s, mask, rows, vidx, pos, live, kl_out, lse_out);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(compact_gather_kernel<__bf16>, dim3((unsigned)rows_alloc), dim3(256), 0, s, vidx, live,
+                       rows_alloc, (const __bf16*)H, d, ids, tlogit, K, (__bf16*)Hc, ids_c, tl_c);
+  else
+    hipLaunchKernelGGL(compact_gather_kernel<float>, dim3((unsigned)rows_alloc), dim3(256), 0, s, vidx, live,
+                       rows_alloc, (const float*)H, d, ids, tlogit, K, (float*)Hc, ids_c, tl_c);
+  return hipGetLastError();
+}
 
 hipError_t launch_mask_count(const uint8_t* mask, int64_t N, void* scal, hipStream_t s) {
   hipLaunchKernelGGL(mask_count_kernel, dim3(1), dim3(1024), 0, s, mask, N, (Scalars*)scal);

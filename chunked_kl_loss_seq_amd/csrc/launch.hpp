@@ -15,25 +15,31 @@ inline int64_t tile_row_stride(int64_t V) { return ((V + 63) / 64) * 4096; }
 // tiled layout, tile rows tile_row_stride(cols) elements apart.
 hipError_t launch_tile_copy(Dtype dt, const void* src, int64_t rows, int64_t cols, void* dst, hipStream_t s);
 
+// With a mask, a chunk is compacted first (launch_compact) and its kernels
+// take `live`: a device int, the number of valid rows, which sit at the front
+// of the chunk's buffers.  Rows at and after it are skipped: no logits, zero
+// gradient rows.  Without a mask `live` is null and every row is computed.
+
 // Logits of one chunk, kept as exp values: per (row n < rows, 128-id slice s)
 // the slice max m and sum of exp(z - m) into part[n][s], and exp(z - m) for
 // every z = H_c[n] . W[v] into P (element type of dt, tiled, tile rows pblk
 // elements apart).
 // W is the tiled copy of the weight (tile_row_stride(d) elements between tile rows).
 hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, hipStream_t s);
+                         int64_t pblk, float2* part, int n_slices, const int* live, hipStream_t s);
 
 // dH partial slabs of one chunk: slab[s][n][j] = sum over the s-th vocabulary
 // split of G[n][v] W[v][j].  G is tiled like P, tile rows gblk elements apart;
 // Wt is the tiled copy of the weight.
 hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,
-                     float* slab, int splits, hipStream_t s);
+                     float* slab, int splits, const int* live, hipStream_t s);
 // dH rows = sum of the slabs in split order, rounded once to the output type.
-hipError_t launch_dh_reduce(Dtype dt, const float* slab, int splits, int64_t rows, int64_t d, void* dH,
-                            hipStream_t s);
+// With pos (compacted chunk), dH row j takes slab row pos[j], or zeros if -1.
+hipError_t launch_dh_reduce(Dtype dt, const float* slab, int splits, int64_t rows, int64_t d, const int* pos,
+                            void* dH, hipStream_t s);
 // dW (+)= G^T H_c over the rows of one chunk; beta = 0 overwrites.
 hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int64_t V, int64_t d, int64_t rows,
-                     float* dW, int beta, hipStream_t s);
+                     float* dW, int beta, const int* live, hipStream_t s);
 
 // k-splits used for the dH contraction of a chunk of `rows` rows.
 int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V);
@@ -47,6 +53,17 @@ hipError_t launch_topk(Dtype dt, const void* x, int64_t N, int64_t V, int64_t K,
 
 // Valid-token count n and scale 1/n (0 if n = 0) into scal (int64 n, float s).
 hipError_t launch_mask_count(const uint8_t* mask, int64_t N, void* scal, hipStream_t s);
+// Compaction of the chunk whose mask, H rows, ids and teacher logits start at
+// the given pointers (`rows` positions): vidx[i] = the chunk row of the i-th
+// valid one, pos[j] = the compact index of row j or -1, *live = the valid
+// count; masked rows' kl_out (and lse_out, if not null) are set to 0; the
+// valid rows of H, ids and logits are gathered to Hc, ids_c, tl_c (chunk
+// buffers of rows_alloc rows), and Hc rows [*live, next multiple of 256) are
+// zeroed.
+hipError_t launch_compact(Dtype dt, const uint8_t* mask, int64_t rows, int64_t rows_alloc, const void* H,
+                          int64_t d, const int32_t* ids, const float* tlogit, int K, int* vidx, int* pos,
+                          int* live, float* kl_out, float* lse_out, void* Hc, int32_t* ids_c, float* tl_c,
+                          hipStream_t s);
 
 // Row pass of one chunk (see kernels_rows.hip).
 struct RowArgs {
@@ -65,6 +82,8 @@ struct RowArgs {
   float* scat;          // [rows, K] exact gradient values at the cached ids
   const float* lse_in;  // [rows] log-normalisers saved by a forward pass, or null: merge the slice pairs
   const float* gscale;  // device scalar multiplying the gradient, or null for 1
+  const int* live;      // compacted chunk: rows at and after *live are skipped; null: none
+  const int* vidx;      // compacted chunk: chunk row of each compacted row (row outputs, lse_in); or null
   float* kl_out;        // [rows] KL (0 for masked rows), or null
   float* lse_out;       // [rows] log-normalisers, or null
   float* zg_dbg;        // optional [rows, K]

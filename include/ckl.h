@@ -74,6 +74,9 @@ typedef enum { CKL_DTYPE_BF16 = 0, CKL_DTYPE_F32 = 1 } ckl_dtype;
  *   out_loss   fp32 device scalar
  *   dH         bf16 [N, d]   gradient of the loss with respect to H (overwritten)
  *   dW         fp32 [V, d]   gradient with respect to W (overwritten)
+ * Masked positions contribute nothing; the rows of a chunk after its last
+ * valid position are skipped (no logits are computed for them), which saves
+ * that work on right-padded inputs.  Their dH rows are written as +0.
  * The pages' interface statement is that a training code only swaps in this
  * loss, fed by the precomputed top-K cache (elseif.net page, adoption paragraph). */
 int ckl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
@@ -88,7 +91,8 @@ int ckl_fwd_bwd_f32(const float* H, const float* W, const int32_t* topk_idx, con
 /* ckl_fwd_bwd / ckl_fwd_bwd_f32 selected by `dtype` (ckl_dtype), with two
  * optional per-position outputs (device, caller-owned, may be NULL):
  *   row_kl   fp32 [N]  KL_r of each position (0 for masked positions)
- *   row_lse  fp32 [N]  logsumexp of the student logits of each position
+ *   row_lse  fp32 [N]  logsumexp of the student logits of each position (0 for
+ *                      masked positions)
  * The loss is the sum of row_kl divided by the valid count. */
 int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
                    const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
@@ -108,6 +112,7 @@ int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_
  *   H, W, topk_idx, topk_logit, mask, N, d, V, K, chunk   as for ckl_fwd_bwd
  *   out_loss   fp32 device scalar
  *   row_lse    fp32 [N] (required)   logsumexp of each position's student logits
+ *                                    (0 for masked positions)
  *   row_kl     fp32 [N] or NULL      KL_r (0 for masked positions)
  * With the same inputs and chunk, loss, row_lse and row_kl are bitwise equal
  * to those of ckl_fwd_bwd_ex. */
@@ -180,7 +185,7 @@ const char* ckl_strerror(int status);
  *   zg_out          fp32 [R, K]  the logits at the teacher ids, rebuilt as m + log exp(z - m)
  *   scatter_ids_out int32 [R, K] the ids the top-K values were scattered to
  *   G_out           [R, V]       gradient, bf16 if g_bf16 else fp32
- *   kl_out, lse_out fp32 [R]     per-row KL (0 for masked rows) and logsumexp
+ *   kl_out, lse_out fp32 [R]     per-row KL and logsumexp (both 0 for masked rows)
  * Synchronises `stream` before returning. */
 int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, const uint8_t* mask, int64_t R,
                    int64_t V, int64_t K, float scale, int g_bf16, float* zg_out, int32_t* scatter_ids_out,

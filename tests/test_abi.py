@@ -41,8 +41,9 @@ def ws_formula(N, d, V, K, C, splits, esz=2):
     tile_rows = -(-C // 64)
     nsl = -(-V // 128)
     wt = -(-V // 64) * (-(-d // 64) * 4096)  # tiled copy of W
+    compact = a(C * d * esz) + 2 * a(C * K * 4) + 2 * a(C * 4)  # masked calls: the compacted chunk
     return (a(wt * esz) + a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
-            + 2 * a(N * 4) + 256)
+            + 2 * a(N * 4) + 256 + compact)
 
 
 def test_plan_explicit_chunk_matches_formula():

@@ -107,7 +107,9 @@ def test_row_pass_gather_scatter_and_gradient(g_bf16):
     S_o = np.exp(Z.astype(np.float64) - lse_o[:, None]) * w[:, None]  # dense part w softmax(z)
     G = out["G"].float().cpu().numpy()
     valid = mask == 1
-    np.testing.assert_allclose(out["lse"].cpu().numpy(), lse_o, rtol=1e-6)
+    # masked rows report a log-normaliser of 0
+    np.testing.assert_allclose(out["lse"].cpu().numpy()[valid], lse_o[valid], rtol=1e-6)
+    assert np.all(out["lse"].cpu().numpy()[~valid] == 0)
     kl_tol = 5e-3 if g_bf16 else 2e-5
     np.testing.assert_allclose(out["kl"].cpu().numpy()[valid], kl_o[valid], rtol=kl_tol, atol=kl_tol)
     assert np.all(out["kl"].cpu().numpy()[~valid] == 0)
@@ -167,7 +169,8 @@ def test_small_ragged_shapes(dtype, shape):
     assert np.all(g["dH"][~valid] == 0)
     assert np.all(g["kl"][~valid] == 0)
     tol = 1e-5 if dtype == "f32" else 3e-3
-    np.testing.assert_allclose(g["lse"], o["lse"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(g["lse"][valid], o["lse"][valid], rtol=tol, atol=tol)
+    assert np.all(g["lse"][~valid] == 0)
     assert rel_fro(g["kl"][valid], o["kl"][valid]) <= (1e-5 if dtype == "f32" else 5e-3)
 
 
@@ -267,7 +270,8 @@ def _sampled_full_size(binding, number, n_sample=48):
     valid = inp["mask"][rows] == 1
     e_kl = rel_fro(g["kl"][rows][valid], o["kl"][valid])
     e_dh = rel_fro(g["dH"][rows], o["dH"])
-    e_lse = float(np.max(np.abs(g["lse"][rows] - o["lse"])))
+    e_lse = float(np.max(np.abs(g["lse"][rows][valid] - o["lse"][valid])))
+    assert np.all(g["lse"][rows][~valid] == 0)
     say(f"[parity {wl.name} sampled] kl {e_kl:.2e} dH rows {e_dh:.2e} lse max abs {e_lse:.2e}")
     assert e_kl <= 2e-3 and e_dh <= 1e-2 and e_lse <= 1e-3
     # the loss is the mean of the per-row KL over valid rows
@@ -372,3 +376,30 @@ def test_seeded_random_shapes(case):
     check(g, o, dtype, f"sweep {case}")
     valid = inp["mask"] == 1
     assert np.all(g["dH"][~valid] == 0)
+
+
+# ------------------------------------------------------------------ masked tails
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_chunk_tails_are_skipped_and_exact(dtype):
+    # right-padded sequences: the rows after each chunk's last valid row are
+    # skipped by every kernel (whole logits and dH tiles, dW k-steps); one
+    # chunk is all padding and one has no padding.  Results must still match
+    # the oracle, masked dH rows are +0, masked rows report KL 0 and lse 0.
+    binding = _need_gpu()
+    N, d, V, K, chunk = 1536, 192, 3000, 40, 512
+    say(f"[case] masked chunk tails {dtype}")
+    inp = WL.small(N, d, V, K, dtype=dtype, ids="uniform", seed=99)
+    m = np.ones(N, dtype=np.uint8)
+    m[512 - 300:512] = 0      # chunk 0: valid rows 0..211, then 300 padded (a whole 256-row tile)
+    m[512:1024] = 0           # chunk 1: all padding
+    m[1024 + 7] = 0           # chunk 2: one masked row inside, valid to the end
+    inp["mask"] = m
+    for c in (chunk, 256, 0):
+        g = run_gpu(binding, inp, dtype, chunk=c, rows=True)
+        o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], want_rows=True)
+        check(g, o, dtype, f"masked tails chunk {c}")
+        valid = m == 1
+        assert np.all(g["dH"][~valid] == 0) and not np.any(np.signbit(g["dH"][~valid]))
+        assert np.all(g["kl"][~valid] == 0) and np.all(g["lse"][~valid] == 0)
+        tol = 1e-5 if dtype == "f32" else 3e-3
+        np.testing.assert_allclose(g["lse"][valid], o["lse"][valid], rtol=tol, atol=tol)
