@@ -74,9 +74,10 @@ typedef enum { CKL_DTYPE_BF16 = 0, CKL_DTYPE_F32 = 1 } ckl_dtype;
  *   out_loss   fp32 device scalar
  *   dH         bf16 [N, d]   gradient of the loss with respect to H (overwritten)
  *   dW         fp32 [V, d]   gradient with respect to W (overwritten)
- * Masked positions contribute nothing; the rows of a chunk after its last
- * valid position are skipped (no logits are computed for them), which saves
- * that work on right-padded inputs.  Their dH rows are written as +0.
+ * Masked positions contribute nothing and cost no GEMM work: with a mask,
+ * each chunk's valid rows are gathered to the front of workspace buffers
+ * before its contractions, so masked rows get no logits.  Their dH rows are
+ * written as +0.
  * The pages' interface statement is that a training code only swaps in this
  * loss, fed by the precomputed top-K cache (elseif.net page, adoption paragraph). */
 int ckl_fwd_bwd(const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
