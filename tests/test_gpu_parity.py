@@ -403,3 +403,27 @@ def test_masked_chunk_tails_are_skipped_and_exact(dtype):
         assert np.all(g["kl"][~valid] == 0) and np.all(g["lse"][~valid] == 0)
         tol = 1e-5 if dtype == "f32" else 3e-3
         np.testing.assert_allclose(g["lse"][valid], o["lse"][valid], rtol=tol, atol=tol)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_heavily_masked_chunks_compact_exactly(dtype):
+    # half the positions masked at random, and chunks whose only valid rows
+    # sit at their very end: the compacted rows come from anywhere in the
+    # chunk, and the compacted row count is far below the chunk's rows
+    binding = _need_gpu()
+    N, d, V, K = 1100, 136, 2500, 33
+    say(f"[case] heavily masked chunks {dtype}")
+    inp = WL.small(N, d, V, K, dtype=dtype, ids="uniform", seed=123)
+    rng = np.random.default_rng(5)
+    m = (rng.random(N) < 0.5).astype(np.uint8)
+    m[300:600] = 0
+    m[590:600] = 1      # chunk 300..599 (with chunk 300): only its last 10 rows are valid
+    inp["mask"] = m
+    for c in (300, 128, 0):
+        g = run_gpu(binding, inp, dtype, chunk=c, rows=True)
+        o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], want_rows=True)
+        check(g, o, dtype, f"heavily masked chunk {c}")
+        valid = m == 1
+        assert np.all(g["dH"][~valid] == 0) and np.all(g["kl"][~valid] == 0) and np.all(g["lse"][~valid] == 0)
+        tol = 1e-5 if dtype == "f32" else 3e-3
+        np.testing.assert_allclose(g["lse"][valid], o["lse"][valid], rtol=tol, atol=tol)
