@@ -15,10 +15,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libckl.so")
 SOURCES = ["ckl_api.hip", "kernels_gemm.hip", "kernels_logits.hip", "kernels_rows.hip", "kernels_topk.hip"]
-# Per-unit flags.  The logits contraction takes the scheduler that favours
-# latency over register pressure (measured: its fragment reads run a whole
-# sub-step of MFMAs ahead); dH and dW measured faster with the default one.
-UNIT_FLAGS = {"kernels_logits.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = "gfx950"
 
 FLAGS = [
@@ -48,7 +44,7 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *FLAGS, *UNIT_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -16,14 +16,17 @@
 //     ds_read_tr16_b64, which hands each lane four k-consecutive 16-bit values
 //     of one column (two reads per bf16 fragment).  fp32 mn-major operands use
 //     ds_read_b32.
-// bf16 operands use v_mfma_f32_32x32x16_bf16; fp32 operands use
-// v_mfma_f32_32x32x2_f32 over the same LDS layout: a fragment holds the
-// 8 k-values k0 + 8h .. k0 + 8h + 7 of lane half h in both cases, and the
-// fp32 path issues 8 MFMAs, one per element, which pair the same k on the A
-// and B side.
+// bf16 operands use v_mfma_f32_32x32x16_bf16 (MS = 32), or for two k-major
+// operands v_mfma_f32_16x16x32_bf16 (MS = 16: the same flops in 16 x 16
+// blocks, which sustain a higher rate under the board's power limit); fp32
+// operands use v_mfma_f32_32x32x2_f32 over the same LDS layout.  A 32-row
+// fragment holds the 8 k-values k0 + 8h .. k0 + 8h + 7 of lane half h, a
+// 16-row one k0 + 8q .. k0 + 8q + 7 of lane quarter q; the fp32 path issues 8
+// MFMAs, one per element, which pair the same k on the A and B side.
 //
-// Accumulator layout of a 32x32 MFMA block (checked on gfx950): lane l, slot r
-// holds D[(r/4)*8 + (l/32)*4 + r%4][l%32].
+// Accumulator layouts (checked on gfx950): in a 32x32 block lane l, slot r
+// holds D[(r/4)*8 + (l/32)*4 + r%4][l%32]; in a 16x16 block lane l, slot r
+// holds D[(l/16)*4 + r][l%16].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -203,7 +206,19 @@ struct SlabDMA {
   static_assert(kBytes % 1024 == 0, "slab must be whole KiB blocks");
 
   uint32_t voff[kNI];
-  uint8_t kd[kNI];  // k offset of this lane's chunk within the slab
+
+  // k offset of this lane's chunk i within the slab (recomputed on tail slabs,
+  // so that it holds no registers through the main loop)
+  __device__ static inline int kdel(int wave, int lane, int i) {
+    const int q = (i * NW + wave) * 1024 + lane * 16;
+    if (KMAJ) {
+      typedef KTile<R, KB> L;
+      const int row = q / KB;
+      const int pc = (q % KB) >> 4;
+      return (pc ^ ((row / L::kRowsPerBankRow) % L::kCPR)) * kEPC;
+    }
+    return q / MNTile<T, R, kBK>::kRowBytes;
+  }
 
   __device__ static inline bool has(int wave, int i) { return kEven || i * NW + wave < kBlocks; }
   static constexpr int kSpare = kEven ? 0 : 1024;  // LDS bytes for the padding loads
@@ -220,7 +235,7 @@ struct SlabDMA {
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const int b = i * NW + wave;
-      int row_mn, kdel;
+      int row_mn, kd;
       int64_t e;
       if (KMAJ) {
         typedef KTile<R, KB> L;
@@ -229,8 +244,8 @@ struct SlabDMA {
         const int pc = (q % KB) >> 4;
         const int c = pc ^ ((row / L::kRowsPerBankRow) % L::kCPR);
         row_mn = row;
-        kdel = c * kEPC;
-        e = elem_offset(o, r0 + row, c0 + kdel) - base;
+        kd = c * kEPC;
+        e = elem_offset(o, r0 + row, c0 + kd) - base;
       } else {
         typedef MNTile<T, R, kBK> L;
         const int q = b * 1024 + lane * 16;
@@ -238,11 +253,10 @@ struct SlabDMA {
         const int pb = q % L::kRowBytes;
         const int lb = (((pb >> 6) ^ L::swz(krow)) << 6) | (pb & 63);
         row_mn = lb / (int)sizeof(T);
-        kdel = krow;
-        e = elem_offset(o, r0 + krow, c0 + row_mn) - base;
+        kd = krow;
+        e = elem_offset(o, r0 + kd, c0 + row_mn) - base;
       }
       voff[i] = (uint32_t)(e * (int64_t)sizeof(T));
-      kd[i] = (uint8_t)kdel;
       if (mn0 + row_mn >= o.mn_ext) voff[i] = kOOB;
     }
   }
@@ -269,12 +283,13 @@ struct SlabDMA {
 
   // Same for a slab that reaches past k_ext: only the first kleft k (none when
   // kleft <= 0) are loaded, the rest read as zeros without touching memory.
-  __device__ inline void issue_tail(uint64_t base, uint32_t lds, int wave, uint32_t spare, int kleft) const {
+  __device__ inline void issue_tail(uint64_t base, uint32_t lds, int wave, int lane, uint32_t spare,
+                                    int kleft) const {
     const i32x4 rs = make_rsrc((const void*)base);
 #pragma unroll
     for (int i = 0; i < kNI; ++i) {
       const bool real = has(wave, i);
-      const uint32_t v = (!real || (int)kd[i] >= kleft) ? kOOB : voff[i];
+      const uint32_t v = (!real || kdel(wave, lane, i) >= kleft) ? kOOB : voff[i];
       dma16(rs, v, real ? lds + (uint32_t)((i * NW + wave) * 1024) : spare);
     }
   }
@@ -341,6 +356,20 @@ __device__ inline typename Frag<T>::type load_frag(const char* lds, int row0, in
   }
 }
 
+// bf16 fragment of 16 rows (row0 .. row0+15) x 32 k (sub-step kk) of a
+// k-major slab for v_mfma_f32_16x16x32_bf16: lane l gets row row0 + l % 16,
+// k = 32 kk + 8 (l / 16) .. + 7.  The 16 lanes one ds_read_b128 serves together
+// read 16 consecutive rows at one chunk, as in the 32-row fragments.
+template <int R, int KB>
+__device__ inline bf16x8 load_frag16(const char* lds, int row0, int kk, int lane) {
+  typedef KTile<R, KB> L;
+  const u32x4 v = *(const u32x4*)(lds + L::off(row0 + (lane & 15), 4 * kk + (lane >> 4)));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ inline f32x4 mfma_block(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 __device__ inline f32x16 mfma_block(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -383,21 +412,34 @@ __device__ inline TileCoord tile_coord(const GemmParams& p) {
 }
 
 // ---------------------------------------------------------------- the kernel
+template <int MS>
+struct AccOf {
+  typedef f32x16 type;  // 32 x 32 block
+};
+template <>
+struct AccOf<16> {
+  typedef f32x4 type;  // 16 x 16 block
+};
+
 // At most 256 VGPRs per lane (two waves per SIMD), so that either one 8-wave
 // or two 4-wave workgroups fit a compute unit; with two workgroups their
-// barriers and epilogues overlap each other's MFMA work.
-template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
+// barriers and epilogues overlap each other's MFMA work.  MS is the MFMA
+// block (32, or 16 for bf16 with both operands k-major).
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS, int MS = 32>
 __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(2))) gemm_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int BK = KB / (int)sizeof(T);
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int SUB = BK / 16;
+  constexpr int FM = WTM / MS, FN = WTN / MS;
+  constexpr int SUB = BK / (MS == 32 ? 16 : 32);
+  constexpr int NR = MS == 32 ? 16 : 4;  // accumulator slots per block
   constexpr int NMF = FM * FN;
   typedef SlabDMA<T, BM, NW, AK, KB> DA;
   typedef SlabDMA<T, BN, NW, BKM, KB> DB;
   constexpr int NIT = DA::kNI + DB::kNI;  // this wave's loads per slab
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(MS == 32 || (MS == 16 && sizeof(T) == 2 && AK && BKM && EPI == EPI_LOGITS),
+                "16 x 16 blocks: bf16 logits (both operands k-major) only");
+  static_assert(WTM % MS == 0 && WTN % MS == 0, "wave tile must be a multiple of the MFMA block");
   static_assert(SUB % 2 == 0 && SUB >= 2, "the pipeline assumes an even sub-step count");
   static_assert(NS >= 2 && (NS - 1) * NIT < 64, "stages in flight must fit the vmcnt counter");
   static_assert(EPI != EPI_LOGITS || WTM == 128, "logit partials are per 128-row slice");
@@ -426,16 +468,24 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     }
   }
 
-  f32x16 acc[FM][FN];
+  typename AccOf<MS>::type acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < NR; ++r) acc[i][j][r] = 0.f;
 
   typedef typename Frag<T>::type FragT;
   FragT fa[2][FM], fb[2][FN];
+  auto lfa = [&](const char* base, int i, int kk, int ln) -> FragT {
+    if constexpr (MS == 16) return load_frag16<BM, KB>(base, wm * WTM + i * 16, kk, ln);
+    else return load_frag<T, BM, AK, KB>(base, wm * WTM + i * 32, kk, ln);
+  };
+  auto lfb = [&](const char* base, int j, int kk, int ln) -> FragT {
+    if constexpr (MS == 16) return load_frag16<BN, KB>(base, wn * WTN + j * 16, kk, ln);
+    else return load_frag<T, BN, BKM, KB>(base, wn * WTN + j * 32, kk, ln);
+  };
   DA da;
   DB db;
   da.init(p.a, m0, wave, lane);
@@ -458,9 +508,9 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
       db.issue_full(b_org + sizeof(T) * (uint64_t)DB::slab_off(p.b, k0), sb_lds, wave, spare);
     } else if (kt < kt_end || !skip) {
       const int kleft = kt < kt_end ? (int)(p.a.k_ext - k0) : 0;
-      da.issue_tail(kt < kt_end ? a_org + sizeof(T) * (uint64_t)DA::slab_off(p.a, k0) : a_org, sa_lds, wave, spare,
+      da.issue_tail(kt < kt_end ? a_org + sizeof(T) * (uint64_t)DA::slab_off(p.a, k0) : a_org, sa_lds, wave, lane, spare,
                     kleft);
-      db.issue_tail(kt < kt_end ? b_org + sizeof(T) * (uint64_t)DB::slab_off(p.b, k0) : b_org, sb_lds, wave, spare,
+      db.issue_tail(kt < kt_end ? b_org + sizeof(T) * (uint64_t)DB::slab_off(p.b, k0) : b_org, sb_lds, wave, lane, spare,
                     kleft);
     }
   };
@@ -478,9 +528,9 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   wait_vmcnt<(NS - 1) * NIT>();
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < FM; ++i) fa[0][i] = load_frag<T, BM, AK, KB>(smem, wm * WTM + i * 32, 0, lane);
+  for (int i = 0; i < FM; ++i) fa[0][i] = lfa(smem, i, 0, lane);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(smem + DA::kBytes, wn * WTN + j * 32, 0, lane);
+  for (int j = 0; j < FN; ++j) fb[0][j] = lfb(smem + DA::kBytes, j, 0, lane);
 
   for (int kt0 = kt_begin; kt0 < kt_end; kt0 += NS) {
 #pragma unroll
@@ -495,16 +545,29 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
       for (int kk = 0; kk < SUB; ++kk) {
         const int fbuf = kk & 1;
+        // With 32 blocks per sub-step the fragment addresses are recomputed
+        // in each sub-step: hoisted out of the loop they would not fit the
+        // register budget.
+        int ln = lane;
+        if constexpr (NMF > 8) asm volatile("" : "+v"(ln));
         if (kk + 1 < SUB) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            fa[fbuf ^ 1][i] = load_frag<T, BM, AK, KB>(sa, wm * WTM + i * 32, kk + 1, lane);
+          for (int i = 0; i < FM; ++i) fa[fbuf ^ 1][i] = lfa(sa, i, kk + 1, ln);
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            fb[fbuf ^ 1][j] = load_frag<T, BN, BKM, KB>(sb, wn * WTN + j * 32, kk + 1, lane);
+          for (int j = 0; j < FN; ++j) fb[fbuf ^ 1][j] = lfb(sb, j, kk + 1, ln);
 #pragma unroll
           for (int q = 0; q < NMF; ++q)
             acc[q / FN][q % FN] = mfma_block(fa[fbuf][q / FN], fb[fbuf][q % FN], acc[q / FN][q % FN]);
+          if constexpr (MS == 16) {
+            // one fragment read every two MFMAs (measured faster than the
+            // scheduler's own order for this loop)
+#pragma unroll
+            for (int q = 0; q < FM + FN; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - 2 * (FM + FN), 0);
+          }
           if constexpr (!AK && !BKM) {
             // both operands come through transpose reads (two per fragment):
             // pin one MFMA, two LDS reads, ... (measured faster for this shape)
@@ -521,9 +584,9 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
           wait_vmcnt<(NS - 2) * NIT>();
           __syncthreads();
 #pragma unroll
-          for (int i = 0; i < FM; ++i) fa[0][i] = load_frag<T, BM, AK, KB>(na, wm * WTM + i * 32, 0, lane);
+          for (int i = 0; i < FM; ++i) fa[0][i] = lfa(na, i, 0, ln);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) fb[0][j] = load_frag<T, BN, BKM, KB>(nb, wn * WTN + j * 32, 0, lane);
+          for (int j = 0; j < FN; ++j) fb[0][j] = lfb(nb, j, 0, ln);
           issue(kt + NS, cur, NS == 2);
 #pragma unroll
           for (int q = NMF / 2; q < NMF; ++q)
@@ -540,7 +603,88 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   const int h = lane >> 5, col = lane & 31;
   const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
   const bool full = (mw + WTM <= p.valid_m) && (nw + WTN <= p.valid_n);
-  if constexpr (EPI == EPI_LOGITS) {
+  if constexpr (MS == 16) {
+    // Logits from 16 x 16 blocks: lane l, slot r of block (i, j) holds the
+    // logit of id mw + 16 i + 4 g + r (g = l / 16) and token nw + 16 j + c
+    // (c = l % 16), so the four lanes c, c + 16, c + 32, c + 48 hold a token's
+    // 128 slice logits, 32 each.  Same outputs as the 32-wide epilogue below.
+    static_assert(WTM == 128 && WTN == 64 && NW * 16384 <= NS * STAGE, "one wave = two 64 x 64 tiles");
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+    const int g = lane >> 4, c = lane & 15;
+    const int slice = (int)(mw / 128);
+    const bool mfull = mw + WTM <= p.valid_m;
+    const int m0lane = (int)mw + 4 * g;
+    const int vm = (int)(p.valid_m < (int64_t)0x7FFFFFFF ? p.valid_m : (int64_t)0x7FFFFFFF);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = nw + 16 * j + c;
+      float mx = -INFINITY, sum = 0.f;
+      if (mfull) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, m0lane + 16 * i + r < vm ? acc[i][j][r] : -INFINITY);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float nmx = -mx * kLog2e;
+      if (mfull) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = slice_exp<T>(acc[i][j][r], mx, nmx);
+            acc[i][j][r] = e;
+            sum += e;
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = slice_exp<T>(acc[i][j][r], mx, nmx);
+            acc[i][j][r] = e;
+            sum += m0lane + 16 * i + r < vm ? e : 0.f;
+          }
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      if (g == 0 && n < p.valid_n && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, sum);
+    }
+    // The exp values leave through this wave's 16 KiB of LDS in the tiles' own
+    // order (token row t of tile i / 4, 16-byte chunks XOR-swizzled by the
+    // row) as 16 coalesced 1 KiB stores, as in the 32-wide epilogue.
+    __syncthreads();
+    char* wl = smem + wave * 16384;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int t = 16 * j + c;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const bf16x4 v = {(__bf16)acc[i][j][0], (__bf16)acc[i][j][1], (__bf16)acc[i][j][2], (__bf16)acc[i][j][3]};
+        const int chunk = 2 * (i & 3) + (g >> 1);  // ids 16 (i % 4) + 4 g .. + 3 of the tile row
+        *(bf16x4*)(wl + (i >> 2) * 8192 + t * 128 + ((chunk ^ (t & 7)) << 4) + 8 * (g & 1)) = v;
+      }
+    }
+    __syncthreads();
+    if (nw < p.valid_n) {
+      T* tile0 = (T*)p.out + (nw >> 6) * p.ldo + (mw >> 6) * 4096;
+#pragma unroll
+      for (int sidx = 0; sidx < 16; ++sidx) {
+        const int idx = sidx * 64 + lane;
+        const int vb = idx >> 9, t = (idx >> 3) & 63, cc = idx & 7;
+        if (mw + 64 * vb < p.valid_m) {
+          const u32x4 v = *(const u32x4*)(wl + vb * 8192 + t * 128 + ((cc ^ (t & 7)) << 4));
+          *(u32x4*)(tile0 + vb * 4096 + t * 64 + cc * 8) = v;
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_LOGITS) {
     // D rows are vocabulary ids (m), columns are tokens (n).  Per token this
     // lane holds 64 of the 128 logits of its wave's slice; its partner lane
     // (lane ^ 32) holds the other 64.  The slice max mx, the exp values
@@ -710,12 +854,12 @@ inline int cdiv64(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // One launch over every tile of p; the grid is rounded up to a multiple of
 // the 8 XCDs so that each XCD gets the same share of the tile order.
-template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS>
+template <typename T, int BM, int BN, int WM, int WN, bool AK, bool BKM, int EPI, int KB, int NS, int MS = 32>
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const int total = p.tiles_m * p.tiles_n * p.splits;
   const int grid = ((total + 7) / 8) * 8;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI, KB, NS>), dim3(grid), dim3(WM * WN * 64), 0, s,
-                     p);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AK, BKM, EPI, KB, NS, MS>), dim3(grid), dim3(WM * WN * 64), 0,
+                     s, p);
   return hipGetLastError();
 }
 
