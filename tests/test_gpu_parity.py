@@ -174,6 +174,28 @@ def test_small_ragged_shapes(dtype, shape):
     assert rel_fro(g["kl"][valid], o["kl"][valid]) <= (1e-5 if dtype == "f32" else 5e-3)
 
 
+# ------------------------------------------------------------------ vocabulary slice and tile edges
+# The logits epilogue keeps a (max, sum) pair per 128-id slice and stores exp
+# values per 64 x 64 tile: vocabularies shorter than one slice, one or two ids
+# past a slice, and token counts that end one row into a tile or a chunk.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(45, 64, 72, 8, 0), (300, 96, 130, 20, 0), (513, 128, 257, 50, 256),
+                                   (129, 32, 383, 383, 0)])
+def test_vocabulary_slice_edges(dtype, shape):
+    binding = _need_gpu()
+    N, d, V, K, chunk = shape
+    say(f"[case] slice edges {dtype} N={N} d={d} V={V} K={K} chunk={chunk}")
+    inp = WL.small(N, d, V, K, dtype=dtype, mask="random5", seed=7 * N + V)
+    g = run_gpu(binding, inp, dtype, chunk=chunk, rows=True)
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], want_rows=True)
+    check(g, o, dtype, f"slice edges {shape}")
+    valid = inp["mask"] == 1
+    tol = 1e-5 if dtype == "f32" else 3e-3
+    np.testing.assert_allclose(g["lse"][valid], o["lse"][valid], rtol=tol, atol=tol)
+    assert np.all(g["lse"][~valid] == 0)
+    assert np.all(g["dH"][~valid] == 0)
+
+
 # ------------------------------------------------------------------ chunk invariance, determinism
 def test_chunk_invariance_and_determinism():
     binding = _need_gpu()
