@@ -42,6 +42,8 @@ def lib():
     L.ckl_fwd_bwd_f32.restype = ctypes.c_int
     L.ckl_fwd_bwd_ex.argtypes = [ctypes.c_int] + L.ckl_fwd_bwd.argtypes[:-1] + [vp, vp, vp]
     L.ckl_fwd_bwd_ex.restype = ctypes.c_int
+    L.ckl_fwd_bwd_noalloc.argtypes = L.ckl_fwd_bwd_ex.argtypes
+    L.ckl_fwd_bwd_noalloc.restype = ctypes.c_int
     L.ckl_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, i64, u64, ctypes.POINTER(i64), ctypes.POINTER(u64)]
     L.ckl_plan.restype = ctypes.c_int
     L.ckl_plan_pass.argtypes = [ctypes.c_int] + L.ckl_plan.argtypes
@@ -104,8 +106,11 @@ def _stream(torch, device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+NOALLOC_MAX_BYTES = 256 << 20  # CKL_NOALLOC_MAX_BYTES
+
+
 def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=None, row_kl=None,
-            row_lse=None):
+            row_lse=None, noalloc=False):
     """Loss, dH and dW of the fused chunked KL loss; tensors on one GPU.
 
     H [N,d] and W [V,d] are both bfloat16 or both float32; ids int32 [N,K];
@@ -113,7 +118,9 @@ def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=No
     (loss 0-dim float32, dH like H, dW float32 [V,d]), all enqueued on the
     current stream.  ``row_kl`` / ``row_lse`` (float32 [N] tensors) receive
     the per-position KL and student logsumexp when given (both 0 for masked
-    positions).
+    positions).  ``noalloc`` calls ckl_fwd_bwd_noalloc, whose workspace is the
+    library's fixed device array (the outputs are still allocated here unless
+    given).
     """
     import torch
 
@@ -136,6 +143,13 @@ def fwd_bwd(H, W, ids, tlogit, mask=None, chunk=0, out_loss=None, dH=None, dW=No
     if dW is None:
         dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     st_dev = _stream(torch, dev)
+    if noalloc:
+        dt = DTYPE_BF16 if H.dtype == torch.bfloat16 else DTYPE_F32
+        st = lib().ckl_fwd_bwd_noalloc(dt, _ptr(H), _ptr(W), _ptr(ids), _ptr(tlogit), _ptr(mask), N, d, V, K,
+                                       int(chunk), _ptr(out_loss), _ptr(dH), _ptr(dW), _ptr(row_kl),
+                                       _ptr(row_lse), st_dev)
+        _check(st, "ckl_fwd_bwd_noalloc")
+        return out_loss, dH, dW
     if row_kl is None and row_lse is None:
         fn = lib().ckl_fwd_bwd if H.dtype == torch.bfloat16 else lib().ckl_fwd_bwd_f32
         st = fn(_ptr(H), _ptr(W), _ptr(ids), _ptr(tlogit), _ptr(mask), N, d, V, K, int(chunk),

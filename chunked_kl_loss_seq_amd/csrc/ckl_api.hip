@@ -15,7 +15,16 @@
 
 using namespace ckl;
 
+// Workspace of ckl_fwd_bwd_noalloc, for callers that cannot allocate device
+// memory.  Each GPU the library runs on holds its own copy of this array until
+// the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: kernels get the address that hipGetSymbolAddress returns
+// for the current device (scratch_ptr below).
+static __device__ __align__(256) char scratch[CKL_NOALLOC_MAX_BYTES];
+
 namespace {
+
+constexpr uint64_t kScratchBytes = CKL_NOALLOC_MAX_BYTES;
 
 constexpr uint64_t kDefaultBudget = 6ull << 30;
 constexpr int64_t kRowStep = 256;
@@ -170,6 +179,29 @@ int get_workspace(int dev, hipStream_t s, uint64_t bytes, void** ptr) {
   return CKL_OK;
 }
 
+// ------------------------------------------------------------------ fixed scratch
+// Address of this device's copy of `scratch` (defined at file scope above),
+// taken once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scr_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_ptr(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return CKL_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scr_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return CKL_EHIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return CKL_OK;
+}
+
 // ------------------------------------------------------------------ timing
 enum Kind { T_LOGITS = 0, T_ROWS, T_DH, T_DHRED, T_DW, T_OTHER, T_TOPK, T_KINDS };
 struct TimingState {
@@ -182,8 +214,8 @@ TimingState g_tm;
 struct Timed {
   int idx = -1;
   hipStream_t s;
-  Timed(int kind, hipStream_t st) : s(st) {
-    if (!g_tm.on) return;
+  Timed(int kind, hipStream_t st, bool enabled = true) : s(st) {
+    if (!g_tm.on || !enabled) return;
     const int i = (int)g_tm.recs.size();
     if (i >= (int)g_tm.pool.size()) {
       hipEvent_t a, b;
@@ -212,10 +244,13 @@ inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0
 //   PASS_FUSED: out_loss, dH, dW (+ optional row_kl, row_lse)
 //   PASS_FWD:   out_loss, row_lse (+ optional row_kl)
 //   PASS_BWD:   lse_in (the forward's row_lse), optional gscale; dH, dW
+// With fixed_ws set, the call runs in the fixed scratch array of this device
+// (budget kScratchBytes) and allocates nothing: no workspace cache, no timing
+// events.
 int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* ids, const float* tlogit,
              const uint8_t* mask, const float* lse_in, const float* gscale, int64_t N, int64_t d, int64_t V,
              int64_t K, int64_t chunk, float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse,
-             hipStream_t stream) {
+             hipStream_t stream, bool fixed_ws = false) {
   const bool want_loss = pass != PASS_BWD, want_grad = pass != PASS_FWD;
   if (!H || !W || !ids || !tlogit) return CKL_EINVAL;
   if (want_loss && !out_loss) return CKL_EINVAL;
@@ -227,15 +262,16 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   if (!aligned(row_kl, 4) || !aligned(row_lse, 4) || !aligned(lse_in, 4) || !aligned(gscale, 4)) return CKL_EINVAL;
   const size_t esz = dt == DT_BF16 ? 2 : 4;
   Layout L;
-  int st = plan_impl(pass, N, d, V, K, chunk, 0, esz, &L);
+  int st = plan_impl(pass, N, d, V, K, chunk, fixed_ws ? kScratchBytes : 0, esz, &L);
   if (st != CKL_OK) return st;
   if ((N + L.C - 1) / L.C > (int64_t)1 << 24) return CKL_EUNSUPPORTED;
 
   int dev = 0;
   CKL_TRY(hipGetDevice(&dev));
   void* ws = nullptr;
-  st = get_workspace(dev, stream, L.total, &ws);
+  st = fixed_ws ? scratch_ptr(dev, &ws) : get_workspace(dev, stream, L.total, &ws);
   if (st != CKL_OK) return st;
+  const bool tm = !fixed_ws;
   char* base = (char*)ws;
   void* Wt = base + L.w_off;
   void* P = base + L.p_off;
@@ -255,7 +291,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   int* pos = (int*)(base + L.pos_off);
 
   {
-    Timed t(T_OTHER, stream);
+    Timed t(T_OTHER, stream, tm);
     CKL_TRY(launch_mask_count(mask, N, scal, stream));
     CKL_TRY(launch_tile_copy(dt, W, V, d, Wt, stream));
   }
@@ -266,7 +302,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
     const float* tl_c = tlogit + r0 * K;
     float* lse_c = pass == PASS_BWD ? nullptr : lse + r0;
     if (live) {
-      Timed t(T_OTHER, stream);
+      Timed t(T_OTHER, stream, tm);
       CKL_TRY(launch_compact(dt, mask + r0, rows, L.C, Hc, d, ids_c, tl_c, (int)K, vidx, pos, live, kl + r0, lse_c,
                              Hcc, idc, tlc, stream));
       Hc = Hcc;
@@ -274,7 +310,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       tl_c = tlc;
     }
     {
-      Timed t(T_LOGITS, stream);
+      Timed t(T_LOGITS, stream, tm);
       CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, live, stream));
     }
     {
@@ -297,7 +333,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       a.gscale = pass == PASS_BWD ? gscale : nullptr;
       a.live = live;
       a.vidx = live ? vidx : nullptr;
-      Timed t(T_ROWS, stream);
+      Timed t(T_ROWS, stream, tm);
       CKL_TRY(launch_row_stats(dt, a, stream));
       if (want_grad) {
         CKL_TRY(launch_dense(dt, a, stream));
@@ -309,21 +345,21 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
     const int64_t cap = (int64_t)L.splits * L.C / rows;  // slab capacity in splits of this chunk
     if (splits > cap) splits = (int)cap;
     {
-      Timed t(T_DH, stream);
+      Timed t(T_DH, stream, tm);
       CKL_TRY(launch_dh(dt, P, L.pblk, Wt, V, d, rows, slab, splits, live, stream));
     }
     {
-      Timed t(T_DHRED, stream);
+      Timed t(T_DHRED, stream, tm);
       CKL_TRY(launch_dh_reduce(dt, slab, splits, rows, d, live ? pos : nullptr, (char*)dH + (size_t)r0 * d * esz,
                                stream));
     }
     {
-      Timed t(T_DW, stream);
+      Timed t(T_DW, stream, tm);
       CKL_TRY(launch_dw(dt, P, L.pblk, Hc, V, d, rows, dW, r0 > 0 ? 1 : 0, live, stream));
     }
   }
   if (want_loss) {
-    Timed t(T_OTHER, stream);
+    Timed t(T_OTHER, stream, tm);
     CKL_TRY(launch_finalize(kl, N, scal, out_loss, stream));
   }
   return CKL_OK;
@@ -365,6 +401,19 @@ int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_
   try {
     return run_impl(PASS_FUSED, to_dt(dtype), H, W, topk_idx, topk_logit, mask, nullptr, nullptr, N, d, V, K, chunk,
                     out_loss, dH, dW, row_kl, row_lse, stream);
+  } catch (...) {
+    return CKL_EHIP;
+  }
+}
+
+int ckl_fwd_bwd_noalloc(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                        const float* topk_logit, const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K,
+                        int64_t chunk, float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse,
+                        hipStream_t stream) {
+  if (!dtype_ok(dtype)) return CKL_EINVAL;
+  try {
+    return run_impl(PASS_FUSED, to_dt(dtype), H, W, topk_idx, topk_logit, mask, nullptr, nullptr, N, d, V, K, chunk,
+                    out_loss, dH, dW, row_kl, row_lse, stream, true);
   } catch (...) {
     return CKL_EHIP;
   }

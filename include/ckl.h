@@ -99,6 +99,32 @@ int ckl_fwd_bwd_ex(int dtype, const void* H, const void* W, const int32_t* topk_
                    const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk,
                    float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse, hipStream_t stream);
 
+/* Largest workspace ckl_fwd_bwd_noalloc can use, in bytes (256 MiB). */
+#define CKL_NOALLOC_MAX_BYTES (256ull << 20)
+
+/* ckl_fwd_bwd_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as ckl_fwd_bwd_ex, except that the
+ * workspace is a fixed array of CKL_NOALLOC_MAX_BYTES in the library's own
+ * device memory, which every GPU the library runs on holds until the process
+ * ends; the call itself allocates and frees nothing.
+ *   - The chunk planner runs with that size as its budget: a shape whose
+ *     smallest workspace (or whose given chunk) does not fit returns
+ *     CKL_EBUDGET before anything is enqueued.  The tiled copy of W alone
+ *     takes V x d x (2 or 4) bytes, so this fits heads up to about
+ *     V x d = 60 M elements in bf16 (e.g. d = 2048, V = 32,000), not the
+ *     largest vocabularies.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind; nothing in it has to start at zero (each buffer is written
+ *     before it is read within a call).  Calls that overlap on one GPU (on
+ *     different streams, or from several threads) race on the array and give
+ *     undefined results: the caller orders them.
+ *   - With the same chunk, the results are bitwise those of ckl_fwd_bwd_ex. */
+int ckl_fwd_bwd_noalloc(int dtype, const void* H, const void* W, const int32_t* topk_idx,
+                        const float* topk_logit, const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K,
+                        int64_t chunk, float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse,
+                        hipStream_t stream);
+
 /* The two-pass form of the same loss, for a training code whose backward runs
  * apart from its forward: the forward keeps one number per position and the
  * backward recomputes each chunk's logits from H and W instead of storing them

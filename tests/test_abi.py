@@ -184,3 +184,21 @@ def test_topk_rejects_bad_arguments_before_any_gpu_call():
     assert L.ckl_topk(0, good, 0, 10, 2, good, good, z) == -1       # N = 0
     assert L.ckl_topk(0, good, 4, 5000, 3000, good, good, z) == -5  # K > 2048
     assert L.ckl_topk(9, good, 4, 10, 2, good, good, z) == -1       # unknown dtype
+
+
+def test_noalloc_rejects_shapes_beyond_its_fixed_workspace():
+    # the planner runs with the fixed array's size as budget: the gpt-oss head
+    # (a 1.16 GB tiled copy of W alone) cannot fit and is refused before any
+    # GPU call; a chunk that does not fit is refused too
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = vp(1 << 20)
+    z = vp(0)
+    assert L.ckl_fwd_bwd_noalloc(0, good, good, good, good, z, 256, 2880, 201088, 100, 0, good, good, good, z, z,
+                                 z) == -3
+    assert L.ckl_fwd_bwd_noalloc(0, good, good, good, good, z, 4096, 2048, 32000, 100, 4096, good, good, good, z,
+                                 z, z) == -3
+    assert L.ckl_fwd_bwd_noalloc(3, good, good, good, good, z, 64, 8, 10, 2, 0, good, good, good, z, z, z) == -1
+    assert B.NOALLOC_MAX_BYTES == 256 << 20
+    _, ws = B.plan(4096, 2048, 32000, 100, budget_bytes=B.NOALLOC_MAX_BYTES)
+    assert ws <= B.NOALLOC_MAX_BYTES
