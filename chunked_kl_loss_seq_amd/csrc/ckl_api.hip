@@ -42,8 +42,10 @@ struct Layout {
   int64_t pblk = 0;     // elements between tile rows of the exp / gradient tiles
   int n_slices = 0;     // (max, sum exp) pairs per row
   int splits = 0;       // k-splits of the dH contraction
+  int ns2 = 0;          // row stride of the id-count table
   uint64_t w_off = 0, p_off = 0, part_off = 0, scat_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0,
-           hc_off = 0, idc_off = 0, tlc_off = 0, vidx_off = 0, pos_off = 0, total = 0;
+           hc_off = 0, idc_off = 0, tlc_off = 0, vidx_off = 0, pos_off = 0, bits_off = 0, pre_off = 0, rank_off = 0,
+           zs_off = 0, total = 0;
 };
 
 Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t C, size_t esz) {
@@ -82,6 +84,17 @@ Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_
   off += align256((uint64_t)C * 4);
   L.pos_off = off;
   off += align256((uint64_t)C * 4);
+  // id tables of the chunk's cached ids: per (row, slice) a 128-bit mask and
+  // a uint16 count, per cached id its rank, and the exact logits by rank
+  L.ns2 = (L.n_slices + 1) & ~1;
+  L.bits_off = off;
+  off += align256((uint64_t)C * L.n_slices * 16);
+  L.pre_off = off;
+  off += align256((uint64_t)C * L.ns2 * 2);
+  L.rank_off = off;
+  off += align256((uint64_t)C * K * 4);
+  L.zs_off = off;
+  off += align256((uint64_t)C * K * 4);
   L.total = off;
   return L;
 }
@@ -102,7 +115,7 @@ int plan_impl(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chu
   if (N <= 0 || d <= 0 || V <= 0 || K <= 0 || chunk < 0) return CKL_EINVAL;
   if (K > V) return CKL_EINVAL;
   if (d % 8 != 0 || K > kMaxK) return CKL_EUNSUPPORTED;
-  if (V > (int64_t)1 << 30 || N > (int64_t)1 << 31 || d > (int64_t)1 << 20) return CKL_EUNSUPPORTED;
+  if (V > (int64_t)1 << 26 || N > (int64_t)1 << 31 || d > (int64_t)1 << 20) return CKL_EUNSUPPORTED;
   budget = budget_from_env(budget);
   if (chunk > 0) {
     const int64_t C = chunk < N ? chunk : N;
@@ -134,8 +147,18 @@ int plan_impl(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chu
   int64_t C = roundup((N + nch - 1) / nch, kRowStep);
   if (C > cmax) C = cmax;
   if (C > N) C = N;
-  *out = make_layout(pass, N, d, V, K, C, esz);
-  return CKL_OK;
+  // The dH split count, and with it the slab bytes, depends on the chunk, so
+  // the workspace is not monotonic in C: the search above only guarantees a
+  // fitting multiple of 256 below the one it returns.  Step down until the
+  // chunk really fits.
+  for (int64_t c = C; c > 0; c = (c % kRowStep) ? c - c % kRowStep : c - kRowStep) {
+    const Layout L = make_layout(pass, N, d, V, K, c, esz);
+    if (L.total <= budget) {
+      *out = L;
+      return CKL_OK;
+    }
+  }
+  return CKL_EBUDGET;
 }
 
 // ------------------------------------------------------------------ workspace cache
@@ -240,6 +263,11 @@ struct Timed {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+bool debug_checks() {
+  const char* e = std::getenv("CKL_DEBUG");
+  return e && e[0] == '1';
+}
+
 // One call of any pass.  Inputs common to all: H, W, ids, tlogit, mask.
 //   PASS_FUSED: out_loss, dH, dW (+ optional row_kl, row_lse)
 //   PASS_FWD:   out_loss, row_lse (+ optional row_kl)
@@ -289,6 +317,14 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   float* tlc = (float*)(base + L.tlc_off);
   int* vidx = (int*)(base + L.vidx_off);
   int* pos = (int*)(base + L.pos_off);
+  IdTables tab{};
+  tab.bits = base + L.bits_off;
+  tab.pre = (const uint16_t*)(base + L.pre_off);
+  tab.ns2 = L.ns2;
+  tab.rank = (const int32_t*)(base + L.rank_off);
+  tab.zs = (float*)(base + L.zs_off);
+  tab.K = (int)K;
+  unsigned* err = (unsigned*)((char*)scal + kErrOffset);
 
   {
     Timed t(T_OTHER, stream, tm);
@@ -310,8 +346,13 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       tl_c = tlc;
     }
     {
+      Timed t(T_ROWS, stream, tm);
+      CKL_TRY(launch_id_tables(ids_c, (int)K, rows, V, live, base + L.bits_off, (uint16_t*)(base + L.pre_off), L.ns2,
+                               (int32_t*)(base + L.rank_off), err, stream));
+    }
+    {
       Timed t(T_LOGITS, stream, tm);
-      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, live, stream));
+      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, &tab, live, stream));
     }
     {
       RowArgs a{};
@@ -333,6 +374,8 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       a.gscale = pass == PASS_BWD ? gscale : nullptr;
       a.live = live;
       a.vidx = live ? vidx : nullptr;
+      a.rank = tab.rank;
+      a.zs = tab.zs;
       Timed t(T_ROWS, stream, tm);
       CKL_TRY(launch_row_stats(dt, a, stream));
       if (want_grad) {
@@ -361,6 +404,15 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   if (want_loss) {
     Timed t(T_OTHER, stream, tm);
     CKL_TRY(launch_finalize(kl, N, scal, out_loss, stream));
+  }
+  // CKL_DEBUG=1: wait for the call and report cached ids outside [0, V) or
+  // repeated within a row (the kernels leave them out, so nothing outside the
+  // buffers was touched, but the results are not those of the definition)
+  if (debug_checks()) {
+    unsigned flags = 0;
+    CKL_TRY(hipMemcpyAsync(&flags, err, sizeof(flags), hipMemcpyDeviceToHost, stream));
+    CKL_TRY(hipStreamSynchronize(stream));
+    if (flags != 0) return CKL_EINVAL;
   }
   return CKL_OK;
 }
@@ -522,22 +574,34 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
     if (!Z || !idx || !tlogit || !zg_out || !scatter_ids_out || !G_out || !kl_out || !lse_out) return CKL_EINVAL;
     if (R <= 0 || V <= 0 || K <= 0 || K > V) return CKL_EINVAL;
     if (K > kMaxK) return CKL_EUNSUPPORTED;
-    if (R > (int64_t)1 << 20 || V > (int64_t)1 << 30) return CKL_EUNSUPPORTED;
+    if (R > (int64_t)1 << 20 || V > (int64_t)1 << 26) return CKL_EUNSUPPORTED;
     const Dtype gdt = g_bf16 ? DT_BF16 : DT_F32;
     const size_t esz = g_bf16 ? 2 : 4;
     const int64_t pblk = tile_row_stride(V);
     const int n_slices = (int)((V + 127) / 128);
+    const int ns2 = (n_slices + 1) & ~1;
     const uint64_t pb = align256((uint64_t)((R + 63) / 64) * pblk * esz);
     const uint64_t qb = align256((uint64_t)R * n_slices * 8);
     const uint64_t sb = align256((uint64_t)R * K * 4);
+    const uint64_t bb = align256((uint64_t)R * n_slices * 16);
+    const uint64_t cb = align256((uint64_t)R * ns2 * 2);
     int dev = 0;
     CKL_TRY(hipGetDevice(&dev));
     void* ws = nullptr;
-    int st = get_workspace(dev, stream, pb + qb + sb, &ws);
+    int st = get_workspace(dev, stream, pb + qb + 3 * sb + bb + cb, &ws);
     if (st != CKL_OK) return st;
-    void* P = ws;
-    float2* part = (float2*)((char*)ws + pb);
-    float* scat = (float*)((char*)ws + pb + qb);
+    char* wsb = (char*)ws;
+    void* P = wsb;
+    float2* part = (float2*)(wsb + pb);
+    float* scat = (float*)(wsb + pb + qb);
+    int32_t* rank = (int32_t*)(wsb + pb + qb + sb);
+    float* zs = (float*)(wsb + pb + qb + 2 * sb);
+    void* bits = wsb + pb + qb + 3 * sb;
+    uint16_t* pre = (uint16_t*)(wsb + pb + qb + 3 * sb + bb);
+    // the id tables the chunk loop builds, and the logits at the cached ids
+    // copied from Z as the logits contraction copies them from its accumulators
+    CKL_TRY(launch_id_tables(idx, (int)K, R, V, nullptr, bits, pre, ns2, rank, nullptr, stream));
+    CKL_TRY(launch_zs_from_z(Z, V, idx, rank, R, (int)K, zs, stream));
     CKL_TRY(launch_partials_from_z(gdt, Z, V, R, V, part, n_slices, P, pblk, stream));
     RowArgs a{};
     a.P = P;
@@ -555,6 +619,8 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
     a.scat = scat;
     a.kl_out = kl_out;
     a.lse_out = lse_out;
+    a.rank = rank;
+    a.zs = zs;
     a.zg_dbg = zg_out;
     a.sid_dbg = scatter_ids_out;
     CKL_TRY(launch_row_stats(gdt, a, stream));

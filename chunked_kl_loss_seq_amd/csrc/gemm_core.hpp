@@ -100,6 +100,17 @@ struct GemmParams {
   // masked.  Logits tiles of those rows return at once, dH tiles of them
   // write zeros without a k-loop, and dW (k = rows) stops its k-loop there.
   const int* live;
+  // EPI_LOGITS, or null: the cached ids of the chunk's rows, as per (row n,
+  // slice s) 128-bit masks id_bits[n][s] and counts id_pre[n][s] (uint16, row
+  // stride ns2) of the row's distinct cached ids below the slice.  The fp32
+  // logit at every masked (id, n) is copied out of the accumulators, before
+  // they become exp values, to zs[n * zk + rank], rank = id_pre[n][s] + the
+  // mask bits below the id.
+  const void* id_bits;
+  const void* id_pre;
+  int ns2;
+  float* zs;
+  int zk;
 };
 
 // ---------------------------------------------------------------- LDS layouts
@@ -180,6 +191,14 @@ __device__ inline uint64_t uniform64(uint64_t v) {
 // scalar write of M0 directly (one wait state), hence the s_nop.
 __device__ inline void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// buffer_load_dword ... lds: lane l's 4 bytes at byte `voff` of the resource
+// go to LDS byte lds_addr + 4 l (same conventions as dma16).
+__device__ inline void dma4(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
                "s"(lds_addr)
                : "memory", "m0");
 }
@@ -411,6 +430,34 @@ __device__ inline TileCoord tile_coord(const GemmParams& p) {
   return tc;
 }
 
+// ---------------------------------------------------------------- cached-id logits
+// Slot r (0..3 or 0..15, varying per lane) of an accumulator block, by selects
+// on constant slots: a register index that differs between lanes would
+// otherwise go through scratch memory.
+__device__ inline float pick4(const f32x4& v, int r) {
+  const float a = (r & 1) ? v[1] : v[0];
+  const float b = (r & 1) ? v[3] : v[2];
+  return (r & 2) ? b : a;
+}
+__device__ inline float pick16(const f32x16& v, int r) {
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = (r & 1) ? v[4 * i + 1] : v[4 * i];
+    const float b = (r & 1) ? v[4 * i + 3] : v[4 * i + 2];
+    q[i] = (r & 2) ? b : a;
+  }
+  const float lo = (r & 4) ? q[1] : q[0];
+  const float hi = (r & 4) ? q[3] : q[2];
+  return (r & 8) ? hi : lo;
+}
+
+// LDS bytes after the stage ring for the tile's id tables: 256 tokens x 2
+// slices x 16-byte masks, then 256 tokens x (count below slice s0, count below
+// slice s0 + 1) as two uint16.
+constexpr int kIdBitsBytes = 256 * 32;
+constexpr int kIdTabBytes = kIdBitsBytes + 256 * 4;
+
 // ---------------------------------------------------------------- the kernel
 template <int MS>
 struct AccOf {
@@ -445,7 +492,10 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
   static_assert(EPI != EPI_LOGITS || WTM == 128, "logit partials are per 128-row slice");
   constexpr int STAGE = DA::kBytes + DB::kBytes;
   constexpr int SPARE = DA::kSpare > DB::kSpare ? DA::kSpare : DB::kSpare;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE + SPARE];
+  constexpr int XOFF = NS * STAGE + SPARE;  // id tables (logits only)
+  constexpr int XBYTES = EPI == EPI_LOGITS ? kIdTabBytes : 0;
+  static_assert(EPI != EPI_LOGITS || (BN == 256 && BM == 256 && NW == 8 && WM == 2), "id tables: 256 x 256 tiles");
+  __shared__ __attribute__((aligned(1024))) char smem[XOFF + XBYTES];
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t spare = lds0 + NS * STAGE;
 
@@ -514,6 +564,28 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
                     kleft);
     }
   };
+
+  // The logits tile's id tables go to LDS ahead of the first slabs, so the
+  // prologue's wait covers them: wave w copies the two slices' masks of tokens
+  // 32 w .. 32 w + 31 (lane l: token 32 w + l / 2, slice s0 + l % 2), waves
+  // 0..3 the count pairs of tokens 64 w .. 64 w + 63.  Tokens past valid_n and
+  // a slice past the vocabulary read as zeros.
+  if constexpr (EPI == EPI_LOGITS) {
+    if (p.id_bits != nullptr) {
+      const int s0 = (int)(m0 >> 7);
+      const uint64_t bbase = uniform64((uint64_t)p.id_bits + ((uint64_t)n0 * p.n_slices + s0) * 16);
+      const int t = 32 * wave + (lane >> 1), sl = lane & 1;
+      const bool ok = n0 + t < p.valid_n && s0 + sl < p.n_slices;
+      dma16(make_rsrc((const void*)bbase), ok ? (uint32_t)(t * p.n_slices + sl) * 16u : kOOB,
+            lds0 + XOFF + (uint32_t)wave * 1024u);
+      if (wave < 4) {
+        const uint64_t pbase = uniform64((uint64_t)p.id_pre + ((uint64_t)n0 * p.ns2 + s0) * 2);
+        const int t2 = 64 * wave + lane;
+        dma4(make_rsrc((const void*)pbase), n0 + t2 < p.valid_n ? (uint32_t)(t2 * p.ns2) * 2u : kOOB,
+             lds0 + XOFF + kIdBitsBytes + (uint32_t)wave * 256u);
+      }
+    }
+  }
 
   // Ring of NS LDS stages.  At the top of iteration kt the stage cur holds
   // slab kt and the other stages hold (or are loading) slabs kt+1 .. kt+NS-1.
@@ -618,6 +690,30 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = nw + 16 * j + c;
+      if (p.id_bits != nullptr) {
+        // logits at the cached ids of token n in this wave's slice: lane
+        // quarter g holds bits 4 g .. 4 g + 3 of every 16 (block i = bit / 16,
+        // slot = bit % 4)
+        const int t = (int)(nw - n0) + 16 * j + c;
+        const u32x4 w = *(const u32x4*)(smem + XOFF + t * 32 + wm * 16);
+        const uint32_t lm = 0x000F000Fu << (4 * g);
+        if (((w.x | w.y | w.z | w.w) & lm) != 0u) {
+          uint32_t run = (*(const uint32_t*)(smem + XOFF + kIdBitsBytes + 4 * t) >> (16 * wm)) & 0xFFFFu;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = w[q];
+            uint32_t m = word & lm;
+            while (m != 0u) {
+              const int b = __builtin_ctz(m);
+              m &= m - 1u;
+              const uint32_t rk = run + (uint32_t)__builtin_popcount(word & ((1u << b) - 1u));
+              const float lo = pick4(acc[2 * q][j], b & 3), hi = pick4(acc[2 * q + 1][j], b & 3);
+              if (rk < (uint32_t)p.zk) p.zs[n * p.zk + rk] = (b & 16) ? hi : lo;
+            }
+            run += (uint32_t)__builtin_popcount(word);
+          }
+        }
+      }
       float mx = -INFINITY, sum = 0.f;
       if (mfull) {
 #pragma unroll
@@ -701,6 +797,31 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = nw + j * 32 + col;
+      if (p.id_bits != nullptr) {
+        // logits at the cached ids of token n in this wave's slice: lane half
+        // h holds bits 4 h .. 4 h + 3 of every 8 (block i = bit / 32, slot
+        // 4 (bit % 32 / 8) + bit % 4)
+        static_assert(FM == 4, "one 32-bit mask word per 32-row block");
+        const int t = (int)(nw - n0) + 32 * j + col;
+        const u32x4 w = *(const u32x4*)(smem + XOFF + t * 32 + wm * 16);
+        const uint32_t lm = 0x0F0F0F0Fu << (4 * h);
+        if (((w.x | w.y | w.z | w.w) & lm) != 0u) {
+          uint32_t run = (*(const uint32_t*)(smem + XOFF + kIdBitsBytes + 4 * t) >> (16 * wm)) & 0xFFFFu;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = w[q];
+            uint32_t m = word & lm;
+            while (m != 0u) {
+              const int b = __builtin_ctz(m);
+              m &= m - 1u;
+              const uint32_t rk = run + (uint32_t)__builtin_popcount(word & ((1u << b) - 1u));
+              const float v = pick16(acc[q][j], ((b >> 3) << 2) | (b & 3));
+              if (rk < (uint32_t)p.zk) p.zs[n * p.zk + rk] = v;
+            }
+            run += (uint32_t)__builtin_popcount(word);
+          }
+        }
+      }
       float mx = -INFINITY, sum = 0.f;
       if (mfull) {
 #pragma unroll

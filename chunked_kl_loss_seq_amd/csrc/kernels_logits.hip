@@ -8,7 +8,8 @@
 namespace ckl {
 
 hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, const int* live, hipStream_t s) {
+                         int64_t pblk, float2* part, int n_slices, const IdTables* tab, const int* live,
+                         hipStream_t s) {
   GemmParams p{};
   p.live = live;
   p.a = Operand{Wt, 0, V, d, tile_row_stride(d)};  // tiled: storage row = vocabulary id, column = d
@@ -26,6 +27,13 @@ hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, in
   p.valid_n = rows;
   p.part = part;
   p.n_slices = n_slices;
+  if (tab != nullptr) {
+    p.id_bits = tab->bits;
+    p.id_pre = tab->pre;
+    p.ns2 = tab->ns2;
+    p.zs = tab->zs;
+    p.zk = tab->K;
+  }
   if (dt == DT_BF16) return launch_gemm<__bf16, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2, 16>(p, s);
   return launch_gemm<float, 256, 256, 2, 4, true, true, EPI_LOGITS, 128, 2>(p, s);
 }

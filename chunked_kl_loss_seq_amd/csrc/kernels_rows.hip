@@ -18,10 +18,15 @@
 // the slice max m_rs and the sum of exp(z - m_rs) (the "slice pairs"), and per
 // logit the value p = exp(z - m_rs) in the element type T of the gradient,
 // laid out in 64 x 64 tiles (tile_off below).  Then, for each chunk:
+//  0. id tables (before the logits GEMM): per row and slice, a 128-bit mask of
+//     the cached ids and the count of cached ids below the slice; per cached id
+//     its rank among the row's distinct ids.  The logits GEMM copies the fp32
+//     logit at each masked position out of its accumulators, before they
+//     become exp values, to zs[r][rank]: the exact logit at each cached id;
 //  1. row_stats: lse_r = merge of the slice pairs; teacher softmax; the cached
-//     ids' logits z = m_rs + log p; KL_r; the per-slice gradient factor
+//     ids' logits z from zs; KL_r; the per-slice gradient factor
 //     f_rs = w_r exp(m_rs - lse_r) (written over the pair's sum); and the exact
-//     gradient value at each cached id, f_rs p - w_r p_T;
+//     gradient value at each cached id, w_r (exp(z - lse_r) - p_T);
 //  2. dense: G = f_rs p over every tile, in place (same element, same type);
 //  3. scatter: G at the cached ids <- the exact values of step 1.
 // With a mask, each chunk is first compacted: its valid rows (H, cached ids
@@ -31,6 +36,7 @@
 // dH rows are written as zeros.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 
 #include "launch.hpp"
 
@@ -48,7 +54,9 @@ struct Scalars {
   long long n_valid;
   float scale;
   float pad;
+  unsigned err;  // at kErrOffset: flags of launch_id_tables, cleared by the valid count
 };
+static_assert(offsetof(Scalars, err) == kErrOffset, "error flags offset");
 
 // Element (row r, column v) of a 64 x 64-tiled matrix whose tile rows are
 // `blk` elements apart.
@@ -151,6 +159,7 @@ __global__ void __launch_bounds__(1024) mask_count_kernel(const uint8_t* __restr
     out->n_valid = t;
     out->scale = t > 0 ? (float)(1.0 / (double)t) : 0.f;
     out->pad = 0.f;
+    out->err = 0u;
   }
 }
 
@@ -225,6 +234,137 @@ __global__ void __launch_bounds__(256) compact_gather_kernel(const int* __restri
   }
 }
 
+// ------------------------------------------------------------------ 0. id tables
+// One workgroup per chunk row r, over its K cached ids:
+//   bits[r][s]  128-bit mask of the cached ids in slice s (ids 128 s .. + 127)
+//   pre[r][s]   number of distinct cached ids below 128 s (row stride ns2;
+//               the padding entry s = n_slices, if any, holds the total)
+//   rank[r][k]  pre[r][s] + the mask bits below id k within its slice: the
+//               place of id k's logit in zs, or -1 for an id outside [0, V)
+// Rows at and past *live (compacted chunk) get empty tables.  The masks of a
+// pass of up to kTabSlices slices are built with LDS atomics; an id whose bit
+// is already set is a repeat within the row.  Flags: 1 = id outside [0, V),
+// 2 = repeated id.
+constexpr int kTabSlices = 2048;
+
+__global__ void __launch_bounds__(kRowThreads) id_table_kernel(const int32_t* __restrict__ ids, int K, int64_t V,
+                                                              int n_slices, int ns2, const int* __restrict__ live,
+                                                              u32x4* __restrict__ bits, uint16_t* __restrict__ pre,
+                                                              int32_t* __restrict__ rank, unsigned* __restrict__ err) {
+  constexpr int NT = kRowThreads;
+  __shared__ u32x4 mb[kTabSlices];
+  __shared__ int sp[kTabSlices];
+  __shared__ int red[NT / 64];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool row_live = live == nullptr || r < *live;
+  int iv[kKPT], rk[kKPT];
+  unsigned flags = 0;
+#pragma unroll
+  for (int q = 0; q < kKPT; ++q) {
+    const int k = tid + q * NT;
+    iv[q] = -1;
+    rk[q] = -1;
+    if (row_live && k < K) {
+      const int id = ids[r * K + k];
+      if (id >= 0 && id < V)
+        iv[q] = id;
+      else
+        flags |= 1u;
+    }
+  }
+  int carry = 0;
+  for (int base = 0; base < n_slices; base += kTabSlices) {
+    const int np = min(kTabSlices, n_slices - base);
+    for (int s = tid; s < np; s += NT) mb[s] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kKPT; ++q) {
+      const int id = iv[q];
+      const int s = (id >> 7) - base;
+      if (id >= 0 && s >= 0 && s < np) {
+        const unsigned bit = 1u << (id & 31);
+        const unsigned old = atomicOr(&((unsigned*)&mb[s])[(id >> 5) & 3], bit);
+        if (old & bit) flags |= 2u;
+      }
+    }
+    __syncthreads();
+    // exclusive prefix of the per-slice counts: thread t takes a run of `per`
+    // slices, then a block scan of the run totals
+    const int per = (np + NT - 1) / NT;
+    const int s0 = tid * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i) {
+      const int s = s0 + i;
+      if (s < np) {
+        const u32x4 w = mb[s];
+        local += __builtin_popcount(w.x) + __builtin_popcount(w.y) + __builtin_popcount(w.z) + __builtin_popcount(w.w);
+      }
+    }
+    int x = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) red[wv] = x;
+    __syncthreads();
+    int before = x - local, total = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      if (i < wv) before += red[i];
+      total += red[i];
+    }
+    int run = carry + before;
+    for (int i = 0; i < per; ++i) {
+      const int s = s0 + i;
+      if (s < np) {
+        sp[s] = run;
+        const u32x4 w = mb[s];
+        run += __builtin_popcount(w.x) + __builtin_popcount(w.y) + __builtin_popcount(w.z) + __builtin_popcount(w.w);
+      }
+    }
+    __syncthreads();
+    for (int s = tid; s < np; s += NT) {
+      bits[r * n_slices + base + s] = mb[s];
+      pre[r * ns2 + base + s] = (uint16_t)sp[s];
+    }
+#pragma unroll
+    for (int q = 0; q < kKPT; ++q) {
+      const int id = iv[q];
+      const int s = (id >> 7) - base;
+      if (id >= 0 && s >= 0 && s < np) {
+        const u32x4 w = mb[s];
+        const int wi = (id >> 5) & 3;
+        const unsigned below = (1u << (id & 31)) - 1u;
+        int c = sp[s] + __builtin_popcount(w[wi] & below);
+        if (wi > 0) c += __builtin_popcount(w.x);
+        if (wi > 1) c += __builtin_popcount(w.y);
+        if (wi > 2) c += __builtin_popcount(w.z);
+        rk[q] = c;
+      }
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0 && n_slices < ns2) pre[r * ns2 + n_slices] = (uint16_t)carry;
+#pragma unroll
+  for (int q = 0; q < kKPT; ++q) {
+    const int k = tid + q * NT;
+    if (k < K) rank[r * K + k] = rk[q];
+  }
+  if (err != nullptr) {
+    // any flag in the workgroup: one atomic from the first wave that has one
+    const unsigned long long any = __ballot(flags != 0);
+    if (any != 0ull) {
+      unsigned f = flags;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
+      if (lane == 0) atomicOr(err, f);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ 1. row statistics
 // One workgroup per token row.
 template <typename T>
@@ -260,7 +400,6 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
   }
 
   // teacher softmax over the cached logits; gather; KL; exact values at the ids
-  const T* P = (const T*)a.P;
   const int K = a.K;
   float tv[kKPT];
   int iv[kKPT];
@@ -288,16 +427,14 @@ __global__ void __launch_bounds__(kRowThreads) row_stats_kernel(RowArgs a) {
     const int k = tid + q * NT;
     if (k < K) {
       const int id = iv[q];
-      const float ms = prow[id >> 7].x;
-      const float pv = to_f(P[tile_off(r, id, a.pblk)]);
-      // z = m + log p; a p that underflowed to zero (z more than about 92
-      // below its slice max in bf16, 103 in fp32) is read as the smallest
-      // positive float
-      const float zg = ms + logf(fmaxf(pv, 1.4e-45f));
+      // the fp32 logit the contraction computed at this id (an id outside
+      // [0, V) has no rank: it is flagged and left out)
+      const int rk = a.rank[r * K + k];
+      const float zg = rk >= 0 ? a.zs[r * K + rk] : 0.f;
       const float lpt = tv[q] - lse_t;
       const float pt = __expf(lpt);
-      klp += pt * (lpt - (zg - lse));
-      a.scat[r * K + k] = valid ? w * __expf(ms - lse) * pv - w * pt : 0.f;
+      if (rk >= 0) klp += pt * (lpt - (zg - lse));
+      a.scat[r * K + k] = (valid && rk >= 0) ? w * __expf(zg - lse) - w * pt : 0.f;
       if (a.zg_dbg) {
         a.zg_dbg[r * K + k] = zg;
         a.sid_dbg[r * K + k] = id;
@@ -364,6 +501,7 @@ __global__ void __launch_bounds__(256) scatter_kernel(RowArgs a) {
   if (a.mask != nullptr && a.mask[r] == 0) return;
   if (a.live != nullptr && r >= *a.live) return;  // past the compacted rows: no ids
   const int id = a.ids[i];
+  if (id < 0 || id >= a.V) return;  // flagged by the id tables; nothing is written
   ((T*)a.P)[tile_off(r, id, a.pblk)] = (T)a.scat[i];
 }
 
@@ -391,6 +529,17 @@ __global__ void __launch_bounds__(128) partials_from_z_kernel(const float* __res
   if ((threadIdx.x & 63) == 0) red[2 + (threadIdx.x >> 6)] = s;
   __syncthreads();
   if (threadIdx.x == 0) part[r * n_slices + slice] = make_float2(m, red[2] + red[3]);
+}
+
+__global__ void __launch_bounds__(256) zs_from_z_kernel(const float* __restrict__ Z, int64_t ldz,
+                                                        const int32_t* __restrict__ ids,
+                                                        const int32_t* __restrict__ rank, int64_t rows, int K,
+                                                        float* __restrict__ zs) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * K) return;
+  const int64_t r = i / K;
+  const int rk = rank[i];
+  if (rk >= 0) zs[r * K + rk] = Z[r * ldz + ids[i]];
 }
 
 template <typename T>
@@ -434,6 +583,24 @@ hipError_t launch_compact(Dtype dt, const uint8_t* mask, int64_t rows, int64_t r
   else
     hipLaunchKernelGGL(compact_gather_kernel<float>, dim3((unsigned)rows_alloc), dim3(256), 0, s, vidx, live,
                        rows_alloc, (const float*)H, d, ids, tlogit, K, (float*)Hc, ids_c, tl_c);
+  return hipGetLastError();
+}
+
+hipError_t launch_id_tables(const int32_t* ids, int K, int64_t rows, int64_t V, const int* live, void* bits,
+                            uint16_t* pre, int ns2, int32_t* rank, unsigned* err, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int n_slices = (int)((V + 127) / 128);
+  hipLaunchKernelGGL(id_table_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, s, ids, K, V, n_slices, ns2, live,
+                     (u32x4*)bits, pre, rank, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_zs_from_z(const float* Z, int64_t ldz, const int32_t* ids, const int32_t* rank, int64_t rows, int K,
+                            float* zs, hipStream_t s) {
+  const int64_t n = rows * K;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zs_from_z_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Z, ldz, ids, rank, rows, K,
+                     zs);
   return hipGetLastError();
 }
 

@@ -20,13 +20,34 @@ hipError_t launch_tile_copy(Dtype dt, const void* src, int64_t rows, int64_t col
 // of the chunk's buffers.  Rows at and after it are skipped: no logits, zero
 // gradient rows.  Without a mask `live` is null and every row is computed.
 
+// Tables of a chunk's cached ids, built by launch_id_tables and read by the
+// logits contraction, which copies the fp32 logit at every cached id out of
+// its accumulators before they become exp values.
+struct IdTables {
+  const void* bits;    // [rows][n_slices] 128-bit masks: bit b of (n, s) = id 128 s + b is cached for row n
+  const uint16_t* pre; // [rows][ns2]: number of distinct cached ids of row n below id 128 s
+  int ns2;             // row stride of pre (n_slices rounded up to even)
+  const int32_t* rank; // [rows][K]: rank of cached id k among its row's distinct ids, -1 if outside [0, V)
+  float* zs;           // [rows][K]: logit of the cached id of rank q at zs[n][q]
+  int K;
+};
+
+// Id tables of `rows` rows of cached ids [rows, K]; with live (compacted
+// chunk), rows at and past *live get empty tables.  Ids outside [0, V) set
+// bit 0 of *err, an id repeated within a row bit 1 (err may be null); both
+// are left out of the tables, so no kernel reads or writes at them.
+hipError_t launch_id_tables(const int32_t* ids, int K, int64_t rows, int64_t V, const int* live, void* bits,
+                            uint16_t* pre, int ns2, int32_t* rank, unsigned* err, hipStream_t s);
+
 // Logits of one chunk, kept as exp values: per (row n < rows, 128-id slice s)
 // the slice max m and sum of exp(z - m) into part[n][s], and exp(z - m) for
 // every z = H_c[n] . W[v] into P (element type of dt, tiled, tile rows pblk
-// elements apart).
+// elements apart).  With tab, the fp32 logit at every cached id also goes to
+// tab->zs.
 // W is the tiled copy of the weight (tile_row_stride(d) elements between tile rows).
 hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, const int* live, hipStream_t s);
+                         int64_t pblk, float2* part, int n_slices, const IdTables* tab, const int* live,
+                         hipStream_t s);
 
 // dH partial slabs of one chunk: slab[s][n][j] = sum over the s-th vocabulary
 // split of G[n][v] W[v][j].  G is tiled like P, tile rows gblk elements apart;
@@ -86,6 +107,8 @@ struct RowArgs {
   const int* vidx;      // compacted chunk: chunk row of each compacted row (row outputs, lse_in); or null
   float* kl_out;        // [rows] KL (0 for masked rows), or null
   float* lse_out;       // [rows] log-normalisers, or null
+  const int32_t* rank;  // [rows, K] rank of each cached id among its row's distinct ids (-1: outside [0, V))
+  const float* zs;      // [rows, K] exact logits of the cached ids, by rank
   float* zg_dbg;        // optional [rows, K]
   int32_t* sid_dbg;     // optional [rows, K]
 };
@@ -97,6 +120,9 @@ hipError_t launch_scatter(Dtype g_dt, const RowArgs& a, hipStream_t s);
 // (row stride ldz); and a tiled matrix copied out to row-major [rows, V].
 hipError_t launch_partials_from_z(Dtype g_dt, const float* Z, int64_t ldz, int64_t rows, int64_t V, float2* part,
                                   int n_slices, void* P, int64_t pblk, hipStream_t s);
+// Debug helper: zs[r][rank[r][k]] = Z[r][ids[r][k]] for the ids of the table.
+hipError_t launch_zs_from_z(const float* Z, int64_t ldz, const int32_t* ids, const int32_t* rank, int64_t rows, int K,
+                            float* zs, hipStream_t s);
 hipError_t launch_untile(Dtype g_dt, const void* P, int64_t pblk, int64_t rows, int64_t V, void* out,
                          hipStream_t s);
 
@@ -104,5 +130,8 @@ hipError_t launch_untile(Dtype g_dt, const void* P, int64_t pblk, int64_t rows, 
 hipError_t launch_finalize(const float* kl, int64_t N, const void* scal, float* out_loss, hipStream_t s);
 
 constexpr int kMaxK = 2048;
+// byte offset, in the device scalar block, of the input-check flags (bit 0: a
+// cached id outside [0, V); bit 1: an id repeated within a row)
+constexpr int kErrOffset = 16;
 
 }  // namespace ckl

@@ -23,6 +23,16 @@
  *   dL/dz_r  = (mask_r / n) (softmax(z_r) - scatter(p_T,r))
  *   dH       = G W,   dW = G^T H                with G the stacked dL/dz_r
  * Temperature 1.  Teacher ids within a row must be distinct and in [0, V).
+ * The logit at each cached id is the very fp32 value the logits contraction
+ * accumulated (copied out before any exponential), so log p_S at the ids is
+ * that of the dense definition to fp32 rounding of the log-normaliser.
+ *
+ * Ids outside [0, V), and repeats within a row, are outside the supported
+ * inputs: no kernel reads or writes at them (they are left out of the loss
+ * and the gradient, so the result is not the definition's), and a device
+ * flag records them.  With the environment variable CKL_DEBUG=1, each loss
+ * call waits for its own kernels and then returns CKL_EINVAL if the flag is
+ * set.
  *
  * Layout and ownership (every call):
  *   - all arrays are row-major and contiguous, in device memory of the device
@@ -58,7 +68,7 @@ typedef enum {
   CKL_ENOMEM = -2,       /* device workspace allocation failed */
   CKL_EBUDGET = -3,      /* no chunk size fits the workspace budget (or the given chunk does not) */
   CKL_EHIP = -4,         /* a HIP runtime call failed */
-  CKL_EUNSUPPORTED = -5  /* d % 8 != 0, K > 2048, or a size beyond 32-bit grid limits */
+  CKL_EUNSUPPORTED = -5  /* d % 8 != 0, K > 2048, V > 2^26, or a size beyond 32-bit grid limits */
 } ckl_status;
 
 typedef enum { CKL_DTYPE_BF16 = 0, CKL_DTYPE_F32 = 1 } ckl_dtype;
@@ -209,7 +219,9 @@ const char* ckl_strerror(int status);
  * is NULL).  Z is first turned into what the logits GEMM leaves in the
  * workspace (per 128-id slice: max m and exp(z - m) in the gradient's element
  * type), then the production row kernels run.  Outputs (device, caller-owned):
- *   zg_out          fp32 [R, K]  the logits at the teacher ids, rebuilt as m + log exp(z - m)
+ *   zg_out          fp32 [R, K]  the logits at the teacher ids as the row pass read them
+ *                                (copied from Z through the same id tables the
+ *                                logits contraction fills: Z[r, id] bit for bit)
  *   scatter_ids_out int32 [R, K] the ids the top-K values were scattered to
  *   G_out           [R, V]       gradient, bf16 if g_bf16 else fp32
  *   kl_out, lse_out fp32 [R]     per-row KL and logsumexp (both 0 for masked rows)

@@ -42,8 +42,10 @@ def ws_formula(N, d, V, K, C, splits, esz=2):
     nsl = -(-V // 128)
     wt = -(-V // 64) * (-(-d // 64) * 4096)  # tiled copy of W
     compact = a(C * d * esz) + 2 * a(C * K * 4) + 2 * a(C * 4)  # masked calls: the compacted chunk
+    ns2 = (nsl + 1) // 2 * 2
+    idtab = a(C * nsl * 16) + a(C * ns2 * 2) + 2 * a(C * K * 4)  # cached-id masks, counts, ranks, exact logits
     return (a(wt * esz) + a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
-            + 2 * a(N * 4) + 256 + compact)
+            + 2 * a(N * 4) + 256 + compact + idtab)
 
 
 def test_plan_explicit_chunk_matches_formula():
@@ -202,3 +204,21 @@ def test_noalloc_rejects_shapes_beyond_its_fixed_workspace():
     assert B.NOALLOC_MAX_BYTES == 256 << 20
     _, ws = B.plan(4096, 2048, 32000, 100, budget_bytes=B.NOALLOC_MAX_BYTES)
     assert ws <= B.NOALLOC_MAX_BYTES
+
+
+def test_planned_workspace_never_exceeds_the_budget():
+    # the dH split count depends on the chunk, so the workspace is not
+    # monotonic in it: the chosen chunk itself must fit, for any N and budget
+    import numpy as np
+
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        N = int(rng.integers(1, 300000))
+        budget = int(rng.choice([2, 3, 4, 6, 8, 12])) << 30
+        try:
+            c, ws = B.plan(N, 2880, 201088, 100, budget_bytes=budget)
+        except B.CklError as e:
+            assert e.status == -3
+            continue
+        assert 0 < c <= N and ws <= budget, (N, budget, c, ws)
+        assert c == N or c % 256 == 0

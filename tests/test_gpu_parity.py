@@ -76,6 +76,13 @@ def check(g, o, dtype, what=""):
     assert ew <= tg, (what, ew)
 
 
+def _fp32_slack(s_at, T, w):
+    """Absolute fp32 rounding allowance of w (exp(z - lse) - p_T) at the cached
+    ids: a few units of 2^-24 of each of its two terms (they may cancel)."""
+    pt = np.exp(O.teacher_log_probs(T)) * np.asarray(w, np.float64)[:, None]
+    return 3e-6 * (np.abs(s_at) + pt) + 1e-30
+
+
 # ------------------------------------------------------------------ row pass alone
 @pytest.mark.parametrize("g_bf16", [True, False])
 def test_row_pass_gather_scatter_and_gradient(g_bf16):
@@ -92,15 +99,11 @@ def test_row_pass_gather_scatter_and_gradient(g_bf16):
     dev = torch.device("cuda:0")
     out = binding.debug_rows(torch.from_numpy(Z).to(dev), torch.from_numpy(ids).to(dev),
                              torch.from_numpy(T).to(dev), torch.from_numpy(mask).to(dev), scale, g_bf16)
-    # index work: the scatter ids are the cached ids, bit for bit
+    # index work: the scatter ids are the cached ids, and the gathered logits
+    # are Z at those ids, bit for bit
     np.testing.assert_array_equal(out["sid"].cpu().numpy(), ids)
-    # the gathered logits are rebuilt as slice max + log p, p = exp(z - max) kept in
-    # the gradient's element type: within one rounding of p (bf16: at most 2^-8
-    # relative, so 2^-8 absolute in log p) plus fp32 exp/log rounding
-    zg = out["zg"].cpu().numpy().astype(np.float64)
-    zt = Z[np.arange(R)[:, None], ids].astype(np.float64)
-    tol_z = 2.0**-8 + 1e-4 if g_bf16 else 1e-5 * (1 + np.abs(zt))
-    assert np.all(np.abs(zg - zt) <= tol_z)
+    zg = out["zg"].cpu().numpy()
+    np.testing.assert_array_equal(zg.view(np.uint32), Z[np.arange(R)[:, None], ids].view(np.uint32))
     kl_o, lse_o, _ = O.row_terms(Z, ids, T)
     w = mask * scale
     G_o = O.logit_grad(Z, ids, T, w)
@@ -110,18 +113,58 @@ def test_row_pass_gather_scatter_and_gradient(g_bf16):
     # masked rows report a log-normaliser of 0
     np.testing.assert_allclose(out["lse"].cpu().numpy()[valid], lse_o[valid], rtol=1e-6)
     assert np.all(out["lse"].cpu().numpy()[~valid] == 0)
-    kl_tol = 5e-3 if g_bf16 else 2e-5
-    np.testing.assert_allclose(out["kl"].cpu().numpy()[valid], kl_o[valid], rtol=kl_tol, atol=kl_tol)
+    # exact gathered logits and fp32 slice sums: the KL is fp32-accurate in
+    # both gradient types
+    np.testing.assert_allclose(out["kl"].cpu().numpy()[valid], kl_o[valid], rtol=2e-5, atol=1e-6)
     assert np.all(out["kl"].cpu().numpy()[~valid] == 0)
     assert np.all(G[~valid] == 0)
     if g_bf16:
-        # p rounded to bf16, then f p (and f p - w p_T at the ids) rounded to
-        # bf16: each rounding at most 2^-8 relative
+        # away from the ids: p rounded to bf16, then f p rounded to bf16 (each
+        # at most 2^-8 relative); at the ids: the fp32 value w (exp(z - lse) -
+        # p_T) rounded once
         assert np.all(np.abs(G - G_o) <= 2.0**-7 * S_o + 2.0**-8 * np.abs(G_o) + 1e-12)
+        rows = np.arange(R)[:, None]
+        at, at_o = G[rows, ids].astype(np.float64), G_o[rows, ids]
+        assert np.all(np.abs(at - at_o) <= 2.0**-8 * np.abs(at_o) + _fp32_slack(S_o[rows, ids], T, w))
     else:
         assert rel_fro(G, G_o) <= 1e-5
     # row sums of the gradient vanish
     assert np.abs(G_o.sum(1)).max() < 1e-15
+
+
+@pytest.mark.parametrize("g_bf16", [True, False])
+def test_row_pass_cached_logit_far_below_its_slice_max(g_bf16):
+    """Cached ids whose logit lies 100, 150 and 300 below the largest logit of
+    their 128-id slice: exp(z - max) underflows in bf16 and fp32 alike, yet the
+    gathered logit, the KL and the gradient at the id are those of the
+    definition (p_S there is far below any float, so G at the id is -w p_T)."""
+    binding = _need_gpu()
+    say(f"[case] row pass far-below-max cached logits g_bf16={g_bf16}")
+    rng = np.random.default_rng(31)
+    R, V, K = 9, 1000, 12
+    Z = rng.standard_normal((R, V)).astype(np.float32)
+    ids = np.stack([rng.permutation(V)[:K] for _ in range(R)]).astype(np.int32)
+    for r in range(R):
+        for k, drop in ((0, 100.0), (3, 150.0), (7, 300.0)):
+            v = ids[r, k]
+            s0 = (v // 128) * 128
+            Z[r, v] = np.float32(Z[r, s0:s0 + 128].max() - drop)
+    T = np.sort(rng.standard_normal((R, K)).astype(np.float32) * 2, axis=1)[:, ::-1].copy()
+    dev = torch.device("cuda:0")
+    out = binding.debug_rows(torch.from_numpy(Z).to(dev), torch.from_numpy(ids).to(dev),
+                             torch.from_numpy(T).to(dev), None, 1.0 / R, g_bf16)
+    zg = out["zg"].cpu().numpy()
+    np.testing.assert_array_equal(zg.view(np.uint32), Z[np.arange(R)[:, None], ids].view(np.uint32))
+    kl_o, lse_o, _ = O.row_terms(Z, ids, T)
+    np.testing.assert_allclose(out["kl"].cpu().numpy(), kl_o, rtol=2e-5, atol=1e-6)
+    w = np.full(R, 1.0 / R)
+    G_o = O.logit_grad(Z, ids, T, w)
+    S_o = np.exp(Z.astype(np.float64) - lse_o[:, None]) * w[:, None]
+    G = out["G"].float().cpu().numpy().astype(np.float64)
+    rows = np.arange(R)[:, None]
+    at, at_o = G[rows, ids], G_o[rows, ids]
+    tol = 2.0**-8 if g_bf16 else 0.0
+    assert np.all(np.abs(at - at_o) <= tol * np.abs(at_o) + _fp32_slack(S_o[rows, ids], T, w))
 
 
 def test_row_pass_gathers_the_requested_columns():
@@ -256,14 +299,79 @@ def test_one_hot_rows_exact_logits():
     inp = {"H": H, "W": W, "ids": ids, "tlogit": T, "mask": np.ones(N, dtype=np.uint8)}
     g = run_gpu(binding, inp, "bf16", chunk=64, rows=True)
     o = O.kl_dense(H, W, ids, T, None, want_rows=True)
-    # the logits are exact on both sides: lse comes from the fp32 slice sums
-    # and agrees to fp32 rounding; the gathered logits pass through the bf16
-    # exp form (one round-to-nearest of p into bf16's 8-bit significand, at
-    # most 2^-8 relative, i.e. 2^-8 absolute in log p), which bounds each
-    # row's KL error by 2^-8 plus fp32 rounding of the sums
+    # the logits are exact on both sides (one product per sum), so the
+    # gathered logits are bit-identical and only the fp32 arithmetic of the
+    # row pass (lse from the fp32 slice sums, the KL sum) separates the rows
     np.testing.assert_allclose(g["lse"], o["lse"], rtol=2e-6)
-    np.testing.assert_allclose(g["kl"], o["kl"], rtol=0, atol=2.0**-8 + 1e-4)
+    np.testing.assert_allclose(g["kl"], o["kl"], rtol=2e-5, atol=2e-6)
     check(g, o, "bf16", "one-hot")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cached_logit_far_below_its_slice_max_end_to_end(dtype):
+    """One-hot H rows and small-integer W, with some cached ids' weight rows
+    at -100 or -160: their logits lie 100+ below the largest logit of their
+    128-id slice, where exp(z - max) underflows, and are exact on both sides.
+    The KL of every row, the loss and the gradients follow the definition."""
+    binding = _need_gpu()
+    say(f"[case] end to end, cached logits 100+ below the slice max, {dtype}")
+    rng = np.random.default_rng(33)
+    N, d, V, K = 150, 32, 1500, 20
+    W = rng.integers(-4, 5, size=(V, d)).astype(np.float32) * 0.25
+    cols = rng.integers(0, d, size=N)
+    H = np.zeros((N, d), dtype=np.float32)
+    H[np.arange(N), cols] = 1.0
+    ids = np.stack([rng.permutation(V)[:K] for _ in range(N)]).astype(np.int32)
+    low = np.unique(ids[:, :3])
+    W[low[: len(low) // 2]] = -100.0
+    W[low[len(low) // 2:]] = -160.0
+    T = np.sort(rng.standard_normal((N, K)).astype(np.float32) * 2, axis=1)[:, ::-1].copy()
+    inp = {"H": H, "W": W, "ids": ids, "tlogit": T, "mask": np.ones(N, dtype=np.uint8)}
+    g = run_gpu(binding, inp, dtype, chunk=64, rows=True)
+    o = O.kl_dense(H, W, ids, T, None, want_rows=True)
+    np.testing.assert_allclose(g["lse"], o["lse"], rtol=2e-6)
+    np.testing.assert_allclose(g["kl"], o["kl"], rtol=2e-5, atol=2e-6)
+    check(g, o, dtype, f"far below slice max {dtype}")
+
+
+@pytest.mark.parametrize("debug", [False, True])
+def test_ids_outside_the_vocabulary_or_repeated_are_left_out_and_flagged(debug):
+    """Cached ids outside [0, V) or repeated within a row are outside the
+    supported inputs.  No kernel reads or writes at them: every other row's KL
+    and dH row are those of the definition.  With CKL_DEBUG=1 the call reports
+    them as CKL_EINVAL."""
+    binding = _need_gpu()
+    say(f"[case] ids out of range / repeated, CKL_DEBUG={int(debug)}")
+    N, d, V, K = 200, 64, 1100, 16
+    inp = WL.small(N, d, V, K, dtype="f32", seed=41)
+    ids = inp["ids"].copy()
+    bad = {3: V, 50: -1, 77: 2**31 - 1, 120: None, 199: V + 127}
+    for r, v in bad.items():
+        ids[r, 5] = ids[r, 2] if v is None else v  # None: a repeat of another cached id
+    H, W, idt, T, mask = to_dev(dict(inp, ids=ids), "f32")
+    kl = torch.empty(N, dtype=torch.float32, device=H.device)
+    old = os.environ.get("CKL_DEBUG")
+    os.environ["CKL_DEBUG"] = "1" if debug else "0"
+    try:
+        if debug:
+            with pytest.raises(binding.CklError) as e:
+                binding.fwd_bwd(H, W, idt, T, None, chunk=64, row_kl=kl)
+            assert e.value.status == -1
+        else:
+            binding.fwd_bwd(H, W, idt, T, None, chunk=64, row_kl=kl)
+    finally:
+        if old is None:
+            del os.environ["CKL_DEBUG"]
+        else:
+            os.environ["CKL_DEBUG"] = old
+    torch.cuda.synchronize()
+    loss, dH, _ = binding.fwd_bwd(H, W, idt, T, None, chunk=64, row_kl=kl)
+    torch.cuda.synchronize()
+    good = np.array([r not in bad for r in range(N)])
+    o = O.kl_rows(inp["H"][good], inp["W"], inp["ids"][good], inp["tlogit"][good], np.full(good.sum(), 1.0 / N))
+    np.testing.assert_allclose(kl.cpu().numpy()[good], o["kl"], rtol=2e-5, atol=1e-6)
+    assert rel_fro(dH.cpu().numpy()[good], o["dH"]) <= 1e-5
+    assert np.all(np.isfinite(dH.cpu().numpy())) and np.isfinite(loss.item())
 
 
 # ------------------------------------------------------------------ named workloads
@@ -315,6 +423,44 @@ def _sampled_full_size(binding, number, n_sample=48):
     say(f"[parity {wl.name}] W^T dW u vs dH^T H u rel {e_id:.2e}")
     assert e_id <= 1e-2
     assert np.all(g["dH"][inp["mask"] == 0] == 0)
+
+
+def test_llama3_head_workload_full_oracle():
+    # 8192 positions (410 masked), d = 3072, V = 128,256: every output against
+    # the dense oracle, at 1024-row chunks and at the planner's chunk
+    binding = _need_gpu()
+    say("[case] llama3 head full size: generating inputs")
+    inp = WL.make(3)
+    say("[case] llama3 head full size: oracle (8192 positions)")
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], block=1024, want_rows=True)
+    valid = inp["mask"] == 1
+    for chunk in (1024, 0):
+        say(f"[case] llama3 head full size: GPU, chunk {chunk}")
+        g = run_gpu(binding, inp, "bf16", chunk=chunk, rows=True)
+        check(g, o, "bf16", f"llama3 head full, chunk {chunk}")
+        assert rel_fro(g["kl"][valid], o["kl"][valid]) <= 2e-3
+        assert np.all(g["dH"][~valid] == 0) and np.all(g["kl"][~valid] == 0)
+
+
+@pytest.mark.parametrize("number", [4, 5])
+def test_gpt_oss_head_4096_row_slice_full_oracle(number):
+    # the first 4096 positions at full d = 2880 and V = 201,088: all of dW
+    # (the half-full last 256-id tile, the quarter-full last 256-column tile)
+    # and dH against the dense oracle, at the planner's chunk and at 1024 rows
+    binding = _need_gpu()
+    say(f"[case] workload {number}, 4096-row slice: generating inputs")
+    inp = WL.make(number, rows=4096)
+    say(f"[case] workload {number}, 4096-row slice: oracle")
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], block=512, want_rows=True)
+    for chunk in (0, 1024):
+        say(f"[case] workload {number}, 4096-row slice: GPU, chunk {chunk}")
+        g = run_gpu(binding, inp, "bf16", chunk=chunk, rows=True)
+        check(g, o, "bf16", f"workload {number} slice, chunk {chunk}")
+        assert rel_fro(g["kl"], o["kl"]) <= 2e-3
+        V = inp["W"].shape[0]
+        tail = slice(V - 128, V)  # the half-full last tile of 256 ids
+        assert rel_fro(g["dW"][tail], o["dW"][tail]) <= 1e-2
+        assert rel_fro(g["dW"][:, 2816:], o["dW"][:, 2816:]) <= 1e-2  # the last 64 columns
 
 
 def test_llama3_head_workload_sampled():
