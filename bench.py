@@ -136,9 +136,33 @@ def cpu_baseline(number, rows):
     O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
     dt = time.perf_counter() - t0
     valid = int(inp["mask"].sum())
+    n = len(inp["mask"])
     return {"value": valid / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {rows} positions of the same workload, float64 NumPy/BLAS dense definition, "
-                      f"{dt:.2f} s wall"}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": (f"first {n} positions of the same workload" if n < WL.WORKLOADS[number].N
+                       else "the whole workload")
+            + f", float64 NumPy/BLAS dense definition, {dt:.2f} s wall"}
+
+
+def cpu_model():
+    """Model name of the host CPU (lscpu, else /proc/cpuinfo), or None."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_topk(args):
@@ -204,6 +228,68 @@ def bench_topk(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_sweep_rows(args):
+    """Workspace against sequence length: the fused call on the first R
+    positions of one workload for each R, with the library's workspace released
+    before each size, so that each size makes its own single allocation.  The
+    pages' point is that the fused loss's memory barely grows with the input
+    grows ("A New Trick...", section "Does this matter for longer documents?")."""
+    import torch
+
+    from chunked_kl_loss_seq_amd import binding
+    from chunked_kl_loss_seq_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    binding.lib()
+    sizes = sorted(int(x) for x in args.sweep_rows.split(","))
+    wl = WL.WORKLOADS[args.workload]
+    if sizes[-1] > wl.N:
+        raise SystemExit(f"workload {args.workload} has {wl.N} positions")
+    log(f"[sweep] generating the first {sizes[-1]} positions of {wl.name}")
+    inp = WL.make(args.workload, rows=sizes[-1])
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    H = torch.from_numpy(inp["H"]).to(dev).to(tdt)
+    W = torch.from_numpy(inp["W"]).to(dev).to(tdt)
+    ids = torch.from_numpy(inp["ids"]).to(dev)
+    T = torch.from_numpy(inp["tlogit"]).to(dev)
+    mask = torch.from_numpy(inp["mask"]).to(dev) if wl.mask != "none" else None
+    del inp
+    d, V, K = wl.d, wl.V, wl.K
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    rows_out = []
+    for R in sizes:
+        C, plan_bytes = binding.plan(R, d, V, K, wl.dtype)
+        binding.release_workspace()
+        torch.cuda.synchronize()
+        free0, _ = torch.cuda.mem_get_info(dev)
+        m = mask[:R] if mask is not None else None
+        binding.fwd_bwd(H[:R], W, ids[:R], T[:R], m, 0, out_loss=loss, dH=dH[:R], dW=dW)
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info(dev)
+        held = binding.workspace_bytes_held()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            binding.fwd_bwd(H[:R], W, ids[:R], T[:R], m, 0, out_loss=loss, dH=dH[:R], dW=dW)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.steps
+        rec = {"tokens": R, "chunk": C, "chunks": -(-R // C), "plan_bytes": plan_bytes, "held_bytes": held,
+               "mem_get_info_drop_bytes": free0 - free1, "ms_per_call": round(ms, 3),
+               "tokens_per_s": round(R / (ms / 1e3), 1), "dense_fp32_logit_grid_bytes": R * V * 4}
+        log(f"[sweep] N={R}: chunk {C} x {rec['chunks']}, plan {plan_bytes / 2**30:.3f} GiB, held "
+            f"{held / 2**30:.3f} GiB, free-memory drop {(free0 - free1) / 2**30:.3f} GiB, {ms:.1f} ms/call")
+        rows_out.append(rec)
+    print(json.dumps({"metric": "fused KL workspace bytes vs sequence length", "workload": wl.name,
+                      "d": d, "V": V, "K": K, "steps": args.steps, "rows": rows_out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,7 +301,12 @@ def main():
                     help="fused: one ckl_fwd_bwd call per step; two-pass: ckl_fwd then ckl_bwd (logits recomputed); "
                          "topk: the teacher top-K cache writer (ckl_topk) over --topk-rows rows")
     ap.add_argument("--topk-rows", type=int, default=8192, help="rows of teacher logits for --variant topk")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="positions in the oracle's timed sample")
+    ap.add_argument("--sweep-rows", default="",
+                    help="comma-separated position counts: run the fused call on that many first positions of "
+                         "--workload for each, the workspace released in between (memory against N)")
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="positions in the oracle's timed sample (default: the whole workload up to 8192 "
+                         "positions, else 4096)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
@@ -246,6 +337,9 @@ def main():
         sys.exit(2)
     if args.variant == "topk":
         bench_topk(args)
+        return
+    if args.sweep_rows:
+        bench_sweep_rows(args)
         return
 
     import numpy as np
@@ -340,8 +434,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the oracle on {args.cpu_rows} positions")
-        cpu = cpu_baseline(args.workload, args.cpu_rows)
+        rows = args.cpu_rows if args.cpu_rows > 0 else (N if N <= 8192 else 4096)
+        log(f"[bench] timing the oracle on {rows} positions")
+        cpu = cpu_baseline(args.workload, rows)
         log(f"[bench] oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     metric = "fused KL fwd+bwd tokens/s + MFMA TFLOP/s % peak; peak workspace GiB"

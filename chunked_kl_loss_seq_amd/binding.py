@@ -44,9 +44,10 @@ def lib():
     L.ckl_fwd_bwd_ex.restype = ctypes.c_int
     L.ckl_fwd_bwd_noalloc.argtypes = L.ckl_fwd_bwd_ex.argtypes
     L.ckl_fwd_bwd_noalloc.restype = ctypes.c_int
-    L.ckl_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, i64, u64, ctypes.POINTER(i64), ctypes.POINTER(u64)]
+    L.ckl_plan.argtypes = [i64, i64, i64, i64, ctypes.c_int, u64, ctypes.POINTER(i64), ctypes.POINTER(u64)]
     L.ckl_plan.restype = ctypes.c_int
-    L.ckl_plan_pass.argtypes = [ctypes.c_int] + L.ckl_plan.argtypes
+    L.ckl_plan_pass.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_int, i64, u64, ctypes.POINTER(i64),
+                                ctypes.POINTER(u64)]
     L.ckl_plan_pass.restype = ctypes.c_int
     L.ckl_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp]
     L.ckl_fwd.restype = ctypes.c_int

@@ -28,6 +28,9 @@ constexpr uint64_t kScratchBytes = CKL_NOALLOC_MAX_BYTES;
 
 constexpr uint64_t kDefaultBudget = 6ull << 30;
 constexpr int64_t kRowStep = 256;
+// Rows per chunk at most: keeps every grid dimension and tile count of a
+// chunk's launches far inside 32 bits.
+constexpr int64_t kMaxChunk = (int64_t)1 << 20;
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 inline int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -119,6 +122,7 @@ int plan_impl(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chu
   budget = budget_from_env(budget);
   if (chunk > 0) {
     const int64_t C = chunk < N ? chunk : N;
+    if (C > kMaxChunk) return CKL_EUNSUPPORTED;
     Layout L = make_layout(pass, N, d, V, K, C, esz);
     if (L.total > budget) return CKL_EBUDGET;
     *out = L;
@@ -129,7 +133,7 @@ int plan_impl(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chu
   if (N <= kRowStep) {
     if (make_layout(pass, N, d, V, K, N, esz).total <= budget) cmax = N;
   } else {
-    int64_t lo = 1, hi = roundup(N, kRowStep) / kRowStep;  // in units of 256 rows
+    int64_t lo = 1, hi = roundup(N < kMaxChunk ? N : kMaxChunk, kRowStep) / kRowStep;  // in units of 256 rows
     if (make_layout(pass, N, d, V, K, kRowStep, esz).total > budget) return CKL_EBUDGET;
     while (lo < hi) {
       const int64_t mid = (lo + hi + 1) / 2;
@@ -528,9 +532,9 @@ int ckl_plan_pass(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int dtyp
   }
 }
 
-int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
-             int64_t* chunk_out, uint64_t* workspace_bytes_out) {
-  return ckl_plan_pass(CKL_PASS_FUSED, N, d, V, K, dtype, chunk, budget_bytes, chunk_out, workspace_bytes_out);
+int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, uint64_t budget_bytes, int64_t* chunk_out,
+             uint64_t* workspace_bytes_out) {
+  return ckl_plan_pass(CKL_PASS_FUSED, N, d, V, K, dtype, 0, budget_bytes, chunk_out, workspace_bytes_out);
 }
 
 void ckl_release_workspace(void) {

@@ -18,8 +18,8 @@ int d_tile(Dtype dt, int64_t d) {
 int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
   // Pick the k-split count (1..8) that best fills whole waves of 256
   // workgroups; each split keeps at least 16 k-steps.
-  const int tiles = cdiv64(rows, 256) * cdiv64(d, d_tile(dt, d));
-  const int ksteps = cdiv64(V, 64);
+  const int64_t tiles = ((rows + 255) / 256) * ((d + d_tile(dt, d) - 1) / d_tile(dt, d));
+  const int64_t ksteps = (V + 63) / 64;
   int best = 1;
   double best_eff = -1.0;
   for (int s = 1; s <= 8; ++s) {

@@ -68,7 +68,8 @@ typedef enum {
   CKL_ENOMEM = -2,       /* device workspace allocation failed */
   CKL_EBUDGET = -3,      /* no chunk size fits the workspace budget (or the given chunk does not) */
   CKL_EHIP = -4,         /* a HIP runtime call failed */
-  CKL_EUNSUPPORTED = -5  /* d % 8 != 0, K > 2048, V > 2^26, or a size beyond 32-bit grid limits */
+  CKL_EUNSUPPORTED = -5  /* d % 8 != 0, K > 2048, V > 2^26, a chunk above 2^20 rows, or a size
+                            beyond 32-bit grid limits */
 } ckl_status;
 
 typedef enum { CKL_DTYPE_BF16 = 0, CKL_DTYPE_F32 = 1 } ckl_dtype;
@@ -186,21 +187,27 @@ typedef enum { CKL_PASS_FUSED = 0, CKL_PASS_FWD = 1, CKL_PASS_BWD = 2 } ckl_pass
 int ckl_topk(int dtype, const void* logits, int64_t N, int64_t V, int64_t K, int32_t* ids_out, float* vals_out,
              hipStream_t stream);
 
-/* Chunk planner (pure host computation, needs no GPU).  The sequence is cut
- * into chunks of C rows so that the loss's own device memory stays bounded
- * independently of N ("A New Trick...", section "Does this matter for longer
- * documents?": peak memory stays almost flat as inputs grow).
- *   chunk         > 0: use min(chunk, N) rows, CKL_EBUDGET if it does not fit;
- *                 0: the largest multiple of 256 rows that fits (or N if
- *                 N < 256), then evened out over the resulting chunk count
+/* Chunk planner of the fused call (pure host computation, needs no GPU).  The
+ * sequence is cut into chunks of C rows so that the loss's own device memory
+ * stays bounded independently of N ("A New Trick...", section "Does this
+ * matter for longer documents?": peak memory barely grows with input length).
+ *   dtype         ckl_dtype of H and W
  *   budget_bytes  0 = CKL_WORKSPACE_BYTES or 6 GiB
- *   chunk_out, workspace_bytes_out  (may be NULL) chosen rows, exact bytes the
- *                 call will allocate for its workspace */
-int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk, uint64_t budget_bytes,
-             int64_t* chunk_out, uint64_t* workspace_bytes_out);
+ *   chunk_out, workspace_bytes_out  (may be NULL) the rows per chunk a call
+ *                 with chunk = 0 uses, and the exact bytes it allocates for its
+ *                 workspace: the largest multiple of 256 rows that fits (or N if
+ *                 N < 256), evened out over the resulting chunk count, then
+ *                 lowered by 256-row steps until it fits (the workspace is not
+ *                 monotonic in the chunk: the dH split count depends on it)
+ * Returns CKL_EBUDGET if not even 256 rows (or N) fit, CKL_EINVAL /
+ * CKL_EUNSUPPORTED for shapes the calls reject. */
+int ckl_plan(int64_t N, int64_t d, int64_t V, int64_t K, int dtype, uint64_t budget_bytes, int64_t* chunk_out,
+             uint64_t* workspace_bytes_out);
 
-/* ckl_plan for one of the calls: pass = ckl_pass (fused = ckl_plan; the
- * forward-only call needs no dH split-K slabs, so it can take longer chunks). */
+/* The planner for one of the calls with a caller-given chunk: pass = ckl_pass
+ * (the forward-only call needs no dH split-K slabs, so it can take longer
+ * chunks); chunk > 0 checks min(chunk, N) rows against the budget
+ * (CKL_EBUDGET if they do not fit), chunk = 0 plans as ckl_plan does. */
 int ckl_plan_pass(int pass, int64_t N, int64_t d, int64_t V, int64_t K, int dtype, int64_t chunk,
                   uint64_t budget_bytes, int64_t* chunk_out, uint64_t* workspace_bytes_out);
 

@@ -222,3 +222,16 @@ def test_planned_workspace_never_exceeds_the_budget():
             continue
         assert 0 < c <= N and ws <= budget, (N, budget, c, ws)
         assert c == N or c % 256 == 0
+
+
+def test_plan_signature_budget_then_outputs():
+    # ckl_plan(N, d, V, K, dtype, budget, &chunk, &bytes): the planner's own
+    # chunk, equal to ckl_plan_pass(fused, ..., chunk = 0, ...)
+    L = B.lib()
+    c = ctypes.c_int64(0)
+    b = ctypes.c_uint64(0)
+    assert L.ckl_plan(32768, 2880, 201088, 100, 0, 0, ctypes.byref(c), ctypes.byref(b)) == 0
+    assert (c.value, b.value) == B.plan(32768, 2880, 201088, 100)
+    assert L.ckl_plan(32768, 2880, 201088, 100, 0, 100 << 20, ctypes.byref(c), ctypes.byref(b)) == -3
+    assert L.ckl_plan(32768, 2880, 201088, 100, 0, 3 << 30, None, None) == 0
+    assert L.ckl_plan(0, 2880, 201088, 100, 0, 0, None, None) == -1

@@ -595,3 +595,35 @@ def test_heavily_masked_chunks_compact_exactly(dtype):
         assert np.all(g["dH"][~valid] == 0) and np.all(g["kl"][~valid] == 0) and np.all(g["lse"][~valid] == 0)
         tol = 1e-5 if dtype == "f32" else 3e-3
         np.testing.assert_allclose(g["lse"][valid], o["lse"][valid], rtol=tol, atol=tol)
+
+
+def test_workspace_allocation_failure_returns_enomem_and_leaves_outputs():
+    # CKL_TEST_FAIL_ALLOC=1 makes the workspace allocation fail: the call
+    # returns CKL_ENOMEM before enqueuing anything, so the outputs keep their
+    # contents, and a later call without it works
+    binding = _need_gpu()
+    say("[case] workspace allocation failure")
+    inp = WL.small(300, 64, 2000, 20, dtype="bf16", mask="random5", seed=2)
+    H, W, ids, T, mask = to_dev(inp, "bf16")
+    loss = torch.full((), 7.0, dtype=torch.float32, device=H.device)
+    dH = torch.full_like(H, 3.0)
+    dW = torch.full((W.shape[0], W.shape[1]), 5.0, dtype=torch.float32, device=H.device)
+    lse = torch.full((H.shape[0],), 9.0, dtype=torch.float32, device=H.device)
+    binding.release_workspace()  # the cache is empty: the next call must allocate
+    assert binding.workspace_bytes_held() == 0
+    os.environ["CKL_TEST_FAIL_ALLOC"] = "1"
+    try:
+        with pytest.raises(binding.CklError) as e:
+            binding.fwd_bwd(H, W, ids, T, mask, chunk=128, out_loss=loss, dH=dH, dW=dW)
+        assert e.value.status == -2
+        with pytest.raises(binding.CklError) as e:
+            binding.fwd(H, W, ids, T, mask, chunk=128, out_loss=loss, row_lse=lse)
+        assert e.value.status == -2
+    finally:
+        del os.environ["CKL_TEST_FAIL_ALLOC"]
+    torch.cuda.synchronize()
+    assert loss.item() == 7.0 and torch.all(dH == 3.0) and torch.all(dW == 5.0) and torch.all(lse == 9.0)
+    assert binding.workspace_bytes_held() == 0
+    g = run_gpu(binding, inp, "bf16", chunk=128)
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
+    check(g, o, "bf16", "after a failed allocation")
