@@ -45,7 +45,7 @@ struct Layout {
   int64_t pblk = 0;     // elements between tile rows of the exp / gradient tiles
   int n_slices = 0;     // (max, sum exp) pairs per row
   int splits = 0;       // k-splits of the dH contraction
-  int ns2 = 0;          // row stride of the id-count table
+  int64_t cpad = 0;     // rows of the id tables (C rounded up to 256)
   uint64_t w_off = 0, p_off = 0, part_off = 0, scat_off = 0, slab_off = 0, kl_off = 0, lse_off = 0, scal_off = 0,
            hc_off = 0, idc_off = 0, tlc_off = 0, vidx_off = 0, pos_off = 0, bits_off = 0, pre_off = 0, rank_off = 0,
            zs_off = 0, total = 0;
@@ -89,11 +89,11 @@ Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_
   off += align256((uint64_t)C * 4);
   // id tables of the chunk's cached ids: per (row, slice) a 128-bit mask and
   // a uint16 count, per cached id its rank, and the exact logits by rank
-  L.ns2 = (L.n_slices + 1) & ~1;
+  L.cpad = roundup(C, 256);
   L.bits_off = off;
-  off += align256((uint64_t)C * L.n_slices * 16);
+  off += align256((uint64_t)id_table_pairs(V) * L.cpad * 32);
   L.pre_off = off;
-  off += align256((uint64_t)C * L.ns2 * 2);
+  off += align256((uint64_t)id_table_pairs(V) * L.cpad * 4);
   L.rank_off = off;
   off += align256((uint64_t)C * K * 4);
   L.zs_off = off;
@@ -323,8 +323,8 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   int* pos = (int*)(base + L.pos_off);
   IdTables tab{};
   tab.bits = base + L.bits_off;
-  tab.pre = (const uint16_t*)(base + L.pre_off);
-  tab.ns2 = L.ns2;
+  tab.pre = base + L.pre_off;
+  tab.cpad = L.cpad;
   tab.rank = (const int32_t*)(base + L.rank_off);
   tab.zs = (float*)(base + L.zs_off);
   tab.K = (int)K;
@@ -351,7 +351,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
     }
     {
       Timed t(T_ROWS, stream, tm);
-      CKL_TRY(launch_id_tables(ids_c, (int)K, rows, V, live, base + L.bits_off, (uint16_t*)(base + L.pre_off), L.ns2,
+      CKL_TRY(launch_id_tables(ids_c, (int)K, rows, V, live, base + L.bits_off, base + L.pre_off, L.cpad,
                                (int32_t*)(base + L.rank_off), err, stream));
     }
     {
@@ -583,12 +583,12 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
     const size_t esz = g_bf16 ? 2 : 4;
     const int64_t pblk = tile_row_stride(V);
     const int n_slices = (int)((V + 127) / 128);
-    const int ns2 = (n_slices + 1) & ~1;
+    const int64_t cpad = roundup(R, 256);
     const uint64_t pb = align256((uint64_t)((R + 63) / 64) * pblk * esz);
     const uint64_t qb = align256((uint64_t)R * n_slices * 8);
     const uint64_t sb = align256((uint64_t)R * K * 4);
-    const uint64_t bb = align256((uint64_t)R * n_slices * 16);
-    const uint64_t cb = align256((uint64_t)R * ns2 * 2);
+    const uint64_t bb = align256((uint64_t)id_table_pairs(V) * cpad * 32);
+    const uint64_t cb = align256((uint64_t)id_table_pairs(V) * cpad * 4);
     int dev = 0;
     CKL_TRY(hipGetDevice(&dev));
     void* ws = nullptr;
@@ -601,10 +601,10 @@ int ckl_debug_rows(const float* Z, const int32_t* idx, const float* tlogit, cons
     int32_t* rank = (int32_t*)(wsb + pb + qb + sb);
     float* zs = (float*)(wsb + pb + qb + 2 * sb);
     void* bits = wsb + pb + qb + 3 * sb;
-    uint16_t* pre = (uint16_t*)(wsb + pb + qb + 3 * sb + bb);
+    void* pre = wsb + pb + qb + 3 * sb + bb;
     // the id tables the chunk loop builds, and the logits at the cached ids
     // copied from Z as the logits contraction copies them from its accumulators
-    CKL_TRY(launch_id_tables(idx, (int)K, R, V, nullptr, bits, pre, ns2, rank, nullptr, stream));
+    CKL_TRY(launch_id_tables(idx, (int)K, R, V, nullptr, bits, pre, cpad, rank, nullptr, stream));
     CKL_TRY(launch_zs_from_z(Z, V, idx, rank, R, (int)K, zs, stream));
     CKL_TRY(launch_partials_from_z(gdt, Z, V, R, V, part, n_slices, P, pblk, stream));
     RowArgs a{};

@@ -100,15 +100,16 @@ struct GemmParams {
   // masked.  Logits tiles of those rows return at once, dH tiles of them
   // write zeros without a k-loop, and dW (k = rows) stops its k-loop there.
   const int* live;
-  // EPI_LOGITS, or null: the cached ids of the chunk's rows, as per (row n,
-  // slice s) 128-bit masks id_bits[n][s] and counts id_pre[n][s] (uint16, row
-  // stride ns2) of the row's distinct cached ids below the slice.  The fp32
-  // logit at every masked (id, n) is copied out of the accumulators, before
-  // they become exp values, to zs[n * zk + rank], rank = id_pre[n][s] + the
-  // mask bits below the id.
+  // EPI_LOGITS, or null: the cached ids of the chunk's rows by 256-id
+  // vocabulary tile p (slices 2p, 2p + 1): 128-bit masks id_bits[p][n][h] of
+  // slice 2p + h, and two uint16 id_pre[p][n] of the row's distinct cached ids
+  // below each slice (row stride id_cpad).  The fp32 logit at every masked
+  // (id, n) is copied out of the accumulators, before they become exp values,
+  // to zs[n * zk + rank], rank = the count below the slice + the mask bits
+  // below the id.
   const void* id_bits;
   const void* id_pre;
-  int ns2;
+  int64_t id_cpad;
   float* zs;
   int zk;
 };
@@ -191,14 +192,6 @@ __device__ inline uint64_t uniform64(uint64_t v) {
 // scalar write of M0 directly (one wait state), hence the s_nop.
 __device__ inline void dma16(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
-               "s"(lds_addr)
-               : "memory", "m0");
-}
-
-// buffer_load_dword ... lds: lane l's 4 bytes at byte `voff` of the resource
-// go to LDS byte lds_addr + 4 l (same conventions as dma16).
-__device__ inline void dma4(const i32x4& rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc),
                "s"(lds_addr)
                : "memory", "m0");
 }
@@ -565,24 +558,22 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     }
   };
 
-  // The logits tile's id tables go to LDS ahead of the first slabs, so the
-  // prologue's wait covers them: wave w copies the two slices' masks of tokens
-  // 32 w .. 32 w + 31 (lane l: token 32 w + l / 2, slice s0 + l % 2), waves
-  // 0..3 the count pairs of tokens 64 w .. 64 w + 63.  Tokens past valid_n and
-  // a slice past the vocabulary read as zeros.
+  // The logits tile's id tables (8 KiB of masks and 1 KiB of count pairs, both
+  // contiguous) go to LDS ahead of the first slabs, so the prologue's wait
+  // covers them: wave w copies the masks of tokens 32 w .. 32 w + 31 (lane l:
+  // token 32 w + l / 2, slice 2 tm + l % 2), wave 0 also the count pairs.
+  // Masks of tokens past valid_n and of a slice past the vocabulary read as
+  // zeros; count pairs are only read where a mask bit is set.
   if constexpr (EPI == EPI_LOGITS) {
     if (p.id_bits != nullptr) {
-      const int s0 = (int)(m0 >> 7);
-      const uint64_t bbase = uniform64((uint64_t)p.id_bits + ((uint64_t)n0 * p.n_slices + s0) * 16);
+      const uint64_t bbase = uniform64((uint64_t)p.id_bits + ((uint64_t)tc.tm * p.id_cpad + n0) * 32);
       const int t = 32 * wave + (lane >> 1), sl = lane & 1;
-      const bool ok = n0 + t < p.valid_n && s0 + sl < p.n_slices;
-      dma16(make_rsrc((const void*)bbase), ok ? (uint32_t)(t * p.n_slices + sl) * 16u : kOOB,
+      const bool ok = n0 + t < p.valid_n && 2 * tc.tm + sl < p.n_slices;
+      dma16(make_rsrc((const void*)bbase), ok ? (uint32_t)(wave * 1024 + lane * 16) : kOOB,
             lds0 + XOFF + (uint32_t)wave * 1024u);
-      if (wave < 4) {
-        const uint64_t pbase = uniform64((uint64_t)p.id_pre + ((uint64_t)n0 * p.ns2 + s0) * 2);
-        const int t2 = 64 * wave + lane;
-        dma4(make_rsrc((const void*)pbase), n0 + t2 < p.valid_n ? (uint32_t)(t2 * p.ns2) * 2u : kOOB,
-             lds0 + XOFF + kIdBitsBytes + (uint32_t)wave * 256u);
+      if (wave == 0) {
+        const uint64_t pbase = uniform64((uint64_t)p.id_pre + ((uint64_t)tc.tm * p.id_cpad + n0) * 4);
+        dma16(make_rsrc((const void*)pbase), (uint32_t)(lane * 16), lds0 + XOFF + kIdBitsBytes);
       }
     }
   }
@@ -687,6 +678,18 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     const bool mfull = mw + WTM <= p.valid_m;
     const int m0lane = (int)mw + 4 * g;
     const int vm = (int)(p.valid_m < (int64_t)0x7FFFFFFF ? p.valid_m : (int64_t)0x7FFFFFFF);
+    // the cached-id masks of this lane's FN tokens in the wave's slice, all
+    // read before the first is needed (one LDS round trip)
+    u32x4 idw[FN];
+    uint32_t idpre[FN];
+    if (p.id_bits != nullptr) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int t = (int)(nw - n0) + 16 * j + c;
+        idw[j] = *(const u32x4*)(smem + XOFF + t * 32 + wm * 16);
+        idpre[j] = *(const uint32_t*)(smem + XOFF + kIdBitsBytes + 4 * t);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = nw + 16 * j + c;
@@ -694,11 +697,10 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
         // logits at the cached ids of token n in this wave's slice: lane
         // quarter g holds bits 4 g .. 4 g + 3 of every 16 (block i = bit / 16,
         // slot = bit % 4)
-        const int t = (int)(nw - n0) + 16 * j + c;
-        const u32x4 w = *(const u32x4*)(smem + XOFF + t * 32 + wm * 16);
+        const u32x4 w = idw[j];
         const uint32_t lm = 0x000F000Fu << (4 * g);
         if (((w.x | w.y | w.z | w.w) & lm) != 0u) {
-          uint32_t run = (*(const uint32_t*)(smem + XOFF + kIdBitsBytes + 4 * t) >> (16 * wm)) & 0xFFFFu;
+          uint32_t run = (idpre[j] >> (16 * wm)) & 0xFFFFu;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t word = w[q];
@@ -794,6 +796,16 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     const bool mfull = mw + WTM <= p.valid_m;
     const int m0lane = (int)mw + h * 4;
     const int vm = (int)(p.valid_m < (int64_t)0x7FFFFFFF ? p.valid_m : (int64_t)0x7FFFFFFF);
+    u32x4 idw[FN];
+    uint32_t idpre[FN];
+    if (p.id_bits != nullptr) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int t = (int)(nw - n0) + 32 * j + col;
+        idw[j] = *(const u32x4*)(smem + XOFF + t * 32 + wm * 16);
+        idpre[j] = *(const uint32_t*)(smem + XOFF + kIdBitsBytes + 4 * t);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t n = nw + j * 32 + col;
@@ -802,11 +814,10 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
         // h holds bits 4 h .. 4 h + 3 of every 8 (block i = bit / 32, slot
         // 4 (bit % 32 / 8) + bit % 4)
         static_assert(FM == 4, "one 32-bit mask word per 32-row block");
-        const int t = (int)(nw - n0) + 32 * j + col;
-        const u32x4 w = *(const u32x4*)(smem + XOFF + t * 32 + wm * 16);
+        const u32x4 w = idw[j];
         const uint32_t lm = 0x0F0F0F0Fu << (4 * h);
         if (((w.x | w.y | w.z | w.w) & lm) != 0u) {
-          uint32_t run = (*(const uint32_t*)(smem + XOFF + kIdBitsBytes + 4 * t) >> (16 * wm)) & 0xFFFFu;
+          uint32_t run = (idpre[j] >> (16 * wm)) & 0xFFFFu;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t word = w[q];

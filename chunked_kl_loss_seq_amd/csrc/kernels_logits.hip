@@ -30,7 +30,7 @@ hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, in
   if (tab != nullptr) {
     p.id_bits = tab->bits;
     p.id_pre = tab->pre;
-    p.ns2 = tab->ns2;
+    p.id_cpad = tab->cpad;
     p.zs = tab->zs;
     p.zk = tab->K;
   }

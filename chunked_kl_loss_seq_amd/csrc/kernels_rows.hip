@@ -235,34 +235,43 @@ __global__ void __launch_bounds__(256) compact_gather_kernel(const int* __restri
 }
 
 // ------------------------------------------------------------------ 0. id tables
-// One workgroup per chunk row r, over its K cached ids:
-//   bits[r][s]  128-bit mask of the cached ids in slice s (ids 128 s .. + 127)
-//   pre[r][s]   number of distinct cached ids below 128 s (row stride ns2;
-//               the padding entry s = n_slices, if any, holds the total)
-//   rank[r][k]  pre[r][s] + the mask bits below id k within its slice: the
-//               place of id k's logit in zs, or -1 for an id outside [0, V)
-// Rows at and past *live (compacted chunk) get empty tables.  The masks of a
-// pass of up to kTabSlices slices are built with LDS atomics; an id whose bit
-// is already set is a repeat within the row.  Flags: 1 = id outside [0, V),
-// 2 = repeated id.
-constexpr int kTabSlices = 2048;
+// Tables of the cached ids of chunk rows, in the layout the logits GEMM reads
+// (pair = two consecutive 128-id slices = one 256-id tile of the vocabulary;
+// rows padded to cpad, a multiple of 256):
+//   bits[pair][row][2]  128-bit mask of the row's cached ids in each slice
+//   pre[pair][row]      two uint16: the number of the row's distinct cached
+//                       ids below each of the pair's two slices (below 128 s
+//                       for a slice s past the vocabulary: the row's total)
+//   rank[row][k]        pre of id k's slice + the mask bits below id k: the
+//                       place of id k's logit in zs, or -1 for an id outside
+//                       [0, V)
+// One workgroup of four waves takes four consecutive rows (wave w: row
+// 4 b + w), so that the four rows' entries of a pair, adjacent in memory, go
+// out as whole 128-byte lines.  The masks of up to kTabSlices slices at a time
+// are built with LDS atomics; an id whose bit is already set is a repeat.
+// Rows at and past *live (compacted chunk) and past `rows` get empty tables.
+// Flags: 1 = id outside [0, V), 2 = repeated id.
+constexpr int kTabSlices = 1024;
+constexpr int kIdsPerLane = kMaxK / 64;
 
-__global__ void __launch_bounds__(kRowThreads) id_table_kernel(const int32_t* __restrict__ ids, int K, int64_t V,
-                                                              int n_slices, int ns2, const int* __restrict__ live,
-                                                              u32x4* __restrict__ bits, uint16_t* __restrict__ pre,
-                                                              int32_t* __restrict__ rank, unsigned* __restrict__ err) {
-  constexpr int NT = kRowThreads;
-  __shared__ u32x4 mb[kTabSlices];
-  __shared__ int sp[kTabSlices];
-  __shared__ int red[NT / 64];
-  const int64_t r = blockIdx.x;
+__global__ void __launch_bounds__(256) id_table_kernel(const int32_t* __restrict__ ids, int K, int64_t V, int n_slices,
+                                                      int64_t cpad, int64_t rows, const int* __restrict__ live,
+                                                      u32x4* __restrict__ bits, uint32_t* __restrict__ pre,
+                                                      int32_t* __restrict__ rank, unsigned* __restrict__ err) {
+  __shared__ u32x4 mb[4][kTabSlices + 4];  // rows 64 bytes of banks apart
+  __shared__ int sp[4][kTabSlices + 1];
+  const int64_t r0 = (int64_t)blockIdx.x * 4;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool row_live = live == nullptr || r < *live;
-  int iv[kKPT], rk[kKPT];
+  const int64_t r = r0 + wv;
+  const bool row_in = r < rows;
+  const bool row_live = row_in && (live == nullptr || r < *live);
+  const int nq = (K + 63) / 64;  // ids per lane in use (uniform)
+  int iv[kIdsPerLane], rk[kIdsPerLane];
   unsigned flags = 0;
 #pragma unroll
-  for (int q = 0; q < kKPT; ++q) {
-    const int k = tid + q * NT;
+  for (int q = 0; q < kIdsPerLane; ++q) {
+    if (q >= nq) break;
+    const int k = lane + 64 * q;
     iv[q] = -1;
     rk[q] = -1;
     if (row_live && k < K) {
@@ -273,33 +282,37 @@ __global__ void __launch_bounds__(kRowThreads) id_table_kernel(const int32_t* __
         flags |= 1u;
     }
   }
-  int carry = 0;
+  int carry = 0;  // this wave's row: distinct ids in the slices before the pass
   for (int base = 0; base < n_slices; base += kTabSlices) {
     const int np = min(kTabSlices, n_slices - base);
-    for (int s = tid; s < np; s += NT) mb[s] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < 4 * kTabSlices; i += 256) mb[i / kTabSlices][i % kTabSlices] = u32x4{0u, 0u, 0u, 0u};
+    // (the 4 padding entries of each row are never read)
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kKPT; ++q) {
+    for (int q = 0; q < kIdsPerLane; ++q) {
+      if (q >= nq) break;
       const int id = iv[q];
       const int s = (id >> 7) - base;
       if (id >= 0 && s >= 0 && s < np) {
         const unsigned bit = 1u << (id & 31);
-        const unsigned old = atomicOr(&((unsigned*)&mb[s])[(id >> 5) & 3], bit);
+        const unsigned old = atomicOr(&((unsigned*)&mb[wv][s])[(id >> 5) & 3], bit);
         if (old & bit) flags |= 2u;
       }
     }
     __syncthreads();
-    // exclusive prefix of the per-slice counts: thread t takes a run of `per`
-    // slices, then a block scan of the run totals
-    const int per = (np + NT - 1) / NT;
-    const int s0 = tid * per;
+    // exclusive prefix of the row's per-slice counts: lane l takes slices
+    // 8 l .. 8 l + 7 of the pass, then a wave scan of the lane totals
+    int cnt[kTabSlices / 64];
     int local = 0;
-    for (int i = 0; i < per; ++i) {
-      const int s = s0 + i;
+#pragma unroll
+    for (int i = 0; i < kTabSlices / 64; ++i) {
+      const int s = lane * (kTabSlices / 64) + i;
+      cnt[i] = 0;
       if (s < np) {
-        const u32x4 w = mb[s];
-        local += __builtin_popcount(w.x) + __builtin_popcount(w.y) + __builtin_popcount(w.z) + __builtin_popcount(w.w);
+        const u32x4 w = mb[wv][s];
+        cnt[i] = __builtin_popcount(w.x) + __builtin_popcount(w.y) + __builtin_popcount(w.z) + __builtin_popcount(w.w);
       }
+      local += cnt[i];
     }
     int x = local;
 #pragma unroll
@@ -307,37 +320,45 @@ __global__ void __launch_bounds__(kRowThreads) id_table_kernel(const int32_t* __
       const int y = __shfl_up(x, o);
       if (lane >= o) x += y;
     }
-    if (lane == 63) red[wv] = x;
-    __syncthreads();
-    int before = x - local, total = 0;
+    const int total = __shfl(x, 63);
+    int run = carry + x - local;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
-      if (i < wv) before += red[i];
-      total += red[i];
+    for (int i = 0; i < kTabSlices / 64; ++i) {
+      const int s = lane * (kTabSlices / 64) + i;
+      if (s < np) sp[wv][s] = run;
+      run += cnt[i];
     }
-    int run = carry + before;
-    for (int i = 0; i < per; ++i) {
-      const int s = s0 + i;
-      if (s < np) {
-        sp[s] = run;
-        const u32x4 w = mb[s];
-        run += __builtin_popcount(w.x) + __builtin_popcount(w.y) + __builtin_popcount(w.z) + __builtin_popcount(w.w);
+    if (lane == 0) sp[wv][np] = carry + total;  // a slice past the pass (or the vocabulary)
+    __syncthreads();
+    // the pass's pairs: the masks of one pair and the four rows are one
+    // 128-byte line, written by 8 consecutive lanes (row i, slice half h);
+    // the count pairs of the four rows are 16 bytes, one lane per pair
+    const int npairs = (np + 1) / 2;
+    for (int e = tid; e < 8 * npairs; e += 256) {
+      const int pl = e >> 3, i = (e >> 1) & 3, h = e & 1;
+      const int sl = 2 * pl + h;
+      bits[((base / 2 + pl) * cpad + r0 + i) * 2 + h] = sl < np ? mb[i][sl] : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int pl = tid; pl < npairs; pl += 256) {
+      const int64_t pr = base / 2 + pl;
+      uint32_t pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sl = 2 * pl;
+        pv[i] = (uint32_t)sp[i][sl] | ((uint32_t)sp[i][sl + 1 < np ? sl + 1 : np] << 16);
       }
-    }
-    __syncthreads();
-    for (int s = tid; s < np; s += NT) {
-      bits[r * n_slices + base + s] = mb[s];
-      pre[r * ns2 + base + s] = (uint16_t)sp[s];
+      *(u32x4*)(pre + pr * cpad + r0) = u32x4{pv[0], pv[1], pv[2], pv[3]};
     }
 #pragma unroll
-    for (int q = 0; q < kKPT; ++q) {
+    for (int q = 0; q < kIdsPerLane; ++q) {
+      if (q >= nq) break;
       const int id = iv[q];
       const int s = (id >> 7) - base;
       if (id >= 0 && s >= 0 && s < np) {
-        const u32x4 w = mb[s];
+        const u32x4 w = mb[wv][s];
         const int wi = (id >> 5) & 3;
         const unsigned below = (1u << (id & 31)) - 1u;
-        int c = sp[s] + __builtin_popcount(w[wi] & below);
+        int c = sp[wv][s] + __builtin_popcount(w[wi] & below);
         if (wi > 0) c += __builtin_popcount(w.x);
         if (wi > 1) c += __builtin_popcount(w.y);
         if (wi > 2) c += __builtin_popcount(w.z);
@@ -347,14 +368,15 @@ __global__ void __launch_bounds__(kRowThreads) id_table_kernel(const int32_t* __
     carry += total;
     __syncthreads();
   }
-  if (tid == 0 && n_slices < ns2) pre[r * ns2 + n_slices] = (uint16_t)carry;
+  if (row_in) {
 #pragma unroll
-  for (int q = 0; q < kKPT; ++q) {
-    const int k = tid + q * NT;
-    if (k < K) rank[r * K + k] = rk[q];
+    for (int q = 0; q < kIdsPerLane; ++q) {
+      if (q >= nq) break;
+      const int k = lane + 64 * q;
+      if (k < K) rank[r * K + k] = rk[q];
+    }
   }
   if (err != nullptr) {
-    // any flag in the workgroup: one atomic from the first wave that has one
     const unsigned long long any = __ballot(flags != 0);
     if (any != 0ull) {
       unsigned f = flags;
@@ -587,11 +609,12 @@ hipError_t launch_compact(Dtype dt, const uint8_t* mask, int64_t rows, int64_t r
 }
 
 hipError_t launch_id_tables(const int32_t* ids, int K, int64_t rows, int64_t V, const int* live, void* bits,
-                            uint16_t* pre, int ns2, int32_t* rank, unsigned* err, hipStream_t s) {
+                            void* pre, int64_t cpad, int32_t* rank, unsigned* err, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (cpad % 256 != 0 || cpad < rows) return hipErrorInvalidValue;
   const int n_slices = (int)((V + 127) / 128);
-  hipLaunchKernelGGL(id_table_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, s, ids, K, V, n_slices, ns2, live,
-                     (u32x4*)bits, pre, rank, err);
+  hipLaunchKernelGGL(id_table_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, ids, K, V, n_slices, cpad,
+                     rows, live, (u32x4*)bits, (uint32_t*)pre, rank, err);
   return hipGetLastError();
 }
 

@@ -23,21 +23,24 @@ hipError_t launch_tile_copy(Dtype dt, const void* src, int64_t rows, int64_t col
 // Tables of a chunk's cached ids, built by launch_id_tables and read by the
 // logits contraction, which copies the fp32 logit at every cached id out of
 // its accumulators before they become exp values.
+// Layout by vocabulary tile: "pair" p = slices 2p, 2p + 1 = ids 256 p .. 256 p + 255.
 struct IdTables {
-  const void* bits;    // [rows][n_slices] 128-bit masks: bit b of (n, s) = id 128 s + b is cached for row n
-  const uint16_t* pre; // [rows][ns2]: number of distinct cached ids of row n below id 128 s
-  int ns2;             // row stride of pre (n_slices rounded up to even)
+  const void* bits;    // [pairs][cpad][2] 128-bit masks: bit b of (p, n, h) = id 256 p + 128 h + b is cached for row n
+  const void* pre;     // [pairs][cpad] two uint16: distinct cached ids of row n below ids 256 p and 256 p + 128
+  int64_t cpad;        // rows of the tables: the chunk's rows rounded up to a multiple of 256
   const int32_t* rank; // [rows][K]: rank of cached id k among its row's distinct ids, -1 if outside [0, V)
   float* zs;           // [rows][K]: logit of the cached id of rank q at zs[n][q]
   int K;
 };
+inline int64_t id_table_pairs(int64_t V) { return (V + 255) / 256; }
 
-// Id tables of `rows` rows of cached ids [rows, K]; with live (compacted
-// chunk), rows at and past *live get empty tables.  Ids outside [0, V) set
-// bit 0 of *err, an id repeated within a row bit 1 (err may be null); both
-// are left out of the tables, so no kernel reads or writes at them.
+// Id tables of `rows` rows of cached ids [rows, K] (cpad >= rows, a multiple
+// of 256); with live (compacted chunk), rows at and past *live get empty
+// tables.  Ids outside [0, V) set bit 0 of *err, an id repeated within a row
+// bit 1 (err may be null); both are left out of the tables, so no kernel
+// reads or writes at them.
 hipError_t launch_id_tables(const int32_t* ids, int K, int64_t rows, int64_t V, const int* live, void* bits,
-                            uint16_t* pre, int ns2, int32_t* rank, unsigned* err, hipStream_t s);
+                            void* pre, int64_t cpad, int32_t* rank, unsigned* err, hipStream_t s);
 
 // Logits of one chunk, kept as exp values: per (row n < rows, 128-id slice s)
 // the slice max m and sum of exp(z - m) into part[n][s], and exp(z - m) for

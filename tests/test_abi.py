@@ -42,8 +42,8 @@ def ws_formula(N, d, V, K, C, splits, esz=2):
     nsl = -(-V // 128)
     wt = -(-V // 64) * (-(-d // 64) * 4096)  # tiled copy of W
     compact = a(C * d * esz) + 2 * a(C * K * 4) + 2 * a(C * 4)  # masked calls: the compacted chunk
-    ns2 = (nsl + 1) // 2 * 2
-    idtab = a(C * nsl * 16) + a(C * ns2 * 2) + 2 * a(C * K * 4)  # cached-id masks, counts, ranks, exact logits
+    cpad, pairs = -(-C // 256) * 256, -(-V // 256)
+    idtab = a(pairs * cpad * 32) + a(pairs * cpad * 4) + 2 * a(C * K * 4)  # cached-id masks, counts, ranks, logits
     return (a(wt * esz) + a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
             + 2 * a(N * 4) + 256 + compact + idtab)
 
