@@ -3,6 +3,10 @@
 // call and for the forward / recomputing-backward pair.
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
+
+#include <cstdarg>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -229,6 +233,59 @@ int scratch_ptr(int dev, void** out) {
   return CKL_OK;
 }
 
+// ------------------------------------------------------------------ tracing
+// CKL_TRACE=1: roctx ranges around each loss call and around each chunk's
+// launches (host enqueue time; `rocprofv3 --marker-trace` records them next to
+// the kernels).  The roctx library is opened at run time, so the library has
+// no link-time dependency on the profiler; without it the ranges are skipped.
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+  bool tried = false;
+};
+Roctx g_roctx;
+std::mutex g_roctx_mu;
+
+bool trace_requested() {
+  const char* e = std::getenv("CKL_TRACE");
+  return e && e[0] == '1';
+}
+
+const Roctx* roctx_api() {
+  std::lock_guard<std::mutex> lk(g_roctx_mu);
+  if (!g_roctx.tried) {
+    g_roctx.tried = true;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+    if (h) {
+      g_roctx.push = (int (*)(const char*))dlsym(h, "roctxRangePushA");
+      g_roctx.pop = (int (*)())dlsym(h, "roctxRangePop");
+      if (!g_roctx.push || !g_roctx.pop) g_roctx.push = nullptr;
+    }
+  }
+  return g_roctx.push ? &g_roctx : nullptr;
+}
+
+struct TraceRange {
+  const Roctx* api = nullptr;
+  explicit TraceRange(const char* fmt, ...) __attribute__((format(printf, 2, 3))) {
+    if (!trace_requested()) return;
+    api = roctx_api();
+    if (!api) return;
+    char buf[192];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    api->push(buf);
+  }
+  ~TraceRange() {
+    if (api) api->pop();
+  }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
+
 // ------------------------------------------------------------------ timing
 enum Kind { T_LOGITS = 0, T_ROWS, T_DH, T_DHRED, T_DW, T_OTHER, T_TOPK, T_KINDS };
 struct TimingState {
@@ -304,6 +361,9 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   st = fixed_ws ? scratch_ptr(dev, &ws) : get_workspace(dev, stream, L.total, &ws);
   if (st != CKL_OK) return st;
   const bool tm = !fixed_ws;
+  static const char* const kPassName[] = {"ckl fused", "ckl forward", "ckl backward"};
+  TraceRange call_range("%s N=%lld d=%lld V=%lld K=%lld chunk=%lld%s%s", kPassName[pass], (long long)N, (long long)d,
+                        (long long)V, (long long)K, (long long)L.C, mask ? " masked" : "", fixed_ws ? " noalloc" : "");
   char* base = (char*)ws;
   void* Wt = base + L.w_off;
   void* P = base + L.p_off;
@@ -337,6 +397,8 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
   }
   for (int64_t r0 = 0; r0 < N; r0 += L.C) {
     const int64_t rows = (N - r0) < L.C ? (N - r0) : L.C;
+    TraceRange chunk_range("chunk %lld: rows %lld-%lld", (long long)(r0 / L.C), (long long)r0,
+                           (long long)(r0 + rows - 1));
     const void* Hc = (const char*)H + (size_t)r0 * d * esz;
     const int32_t* ids_c = ids + r0 * K;
     const float* tl_c = tlogit + r0 * K;

@@ -45,6 +45,11 @@
  *   - the library holds one grow-only device workspace per (device, stream),
  *     sized by ckl_plan; ckl_release_workspace frees them all.
  *
+ * Environment: CKL_WORKSPACE_BYTES (workspace budget, default 6 GiB);
+ * CKL_DEBUG=1 (input checks reported by the call, see above); CKL_TRACE=1
+ * (roctx ranges around every loss call and every chunk, for rocprofv3
+ * --marker-trace; skipped if no roctx library can be opened).
+ *
  * Errors: arguments that are invalid or not supported are reported before
  * anything is enqueued, and the outputs are untouched.  A HIP failure returns
  * CKL_EHIP or CKL_ENOMEM and leaves the outputs undefined; since every call

@@ -627,3 +627,20 @@ def test_workspace_allocation_failure_returns_enomem_and_leaves_outputs():
     g = run_gpu(binding, inp, "bf16", chunk=128)
     o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
     check(g, o, "bf16", "after a failed allocation")
+
+
+def test_trace_ranges_leave_results_unchanged():
+    # CKL_TRACE=1 wraps every call and chunk in roctx ranges (host side only):
+    # the results are bitwise those of an untraced call
+    binding = _need_gpu()
+    say("[case] CKL_TRACE=1")
+    inp = WL.small(500, 128, 3000, 40, dtype="bf16", mask="random5", seed=44)
+    base = run_gpu(binding, inp, "bf16", chunk=128)
+    os.environ["CKL_TRACE"] = "1"
+    try:
+        traced = run_gpu(binding, inp, "bf16", chunk=128)
+    finally:
+        del os.environ["CKL_TRACE"]
+    assert traced["loss"] == base["loss"]
+    np.testing.assert_array_equal(traced["dH"], base["dH"])
+    np.testing.assert_array_equal(traced["dW"], base["dW"])
