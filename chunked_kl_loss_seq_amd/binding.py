@@ -320,14 +320,25 @@ class _FusedKL:
                 @staticmethod
                 def forward(ctx, H, W, ids, tlogit, mask, chunk):
                     loss, dH, dW = fwd_bwd(H.contiguous(), W.contiguous(), ids, tlogit, mask, chunk)
-                    ctx.save_for_backward(dH, dW)
+                    # kept as plain attributes (not saved tensors): backward
+                    # scales them in place, once
+                    ctx.grads = (dH, dW)
                     ctx.w_dtype = W.dtype
                     return loss
 
                 @staticmethod
                 def backward(ctx, g):
-                    dH, dW = ctx.saved_tensors
-                    return (g * dH).to(dH.dtype), (g * dW).to(ctx.w_dtype), None, None, None, None
+                    if ctx.grads is None:
+                        raise RuntimeError("fused_kl: its gradients were computed once, in the forward call, "
+                                           "and have been used; a second backward needs a new forward call")
+                    dH, dW = ctx.grads
+                    ctx.grads = None
+                    # in place: no second copy of the fp32 [V, d] gradient (a
+                    # bf16 W still gets a bf16 gradient, as autograd requires)
+                    g = g.to(torch.float32)
+                    dH.mul_(g)
+                    dW.mul_(g)
+                    return dH, dW if ctx.w_dtype == torch.float32 else dW.to(ctx.w_dtype), None, None, None, None
 
             cls._fn = FusedKL
         return cls._fn

@@ -197,3 +197,22 @@ def test_two_pass_gpt_oss_head_planner_chunks_bitwise():
     inp = WL.make(4)
     say(f"[case] two-pass vs fused, full-size {wl.name}: GPU calls")
     assert_bitwise(*fused_and_two_pass(binding, inp, "bf16", chunk=0, fwd_chunk=0))
+
+
+def test_fused_wrapper_scales_in_place_and_refuses_a_second_backward():
+    # the fused wrapper's gradients were computed in the forward call; its
+    # backward scales them in place by the upstream gradient, once
+    binding = _need_gpu()
+    say("[case] autograd: fused_kl backward twice")
+    inp = WL.small(200, 64, 1500, 30, dtype="f32", seed=6)
+    H, W, ids, T, _ = to_dev(inp, "f32")
+    H.requires_grad_(True)
+    W.requires_grad_(True)
+    loss = binding.fused_kl(H, W, ids, T, None, 64)
+    (2.0 * loss).backward(retain_graph=True)
+    torch.cuda.synchronize()
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], None)
+    assert rel_fro(H.grad.cpu().numpy(), 2.0 * o["dH"]) <= 1e-5
+    assert rel_fro(W.grad.cpu().numpy(), 2.0 * o["dW"]) <= 1e-5
+    with pytest.raises(RuntimeError, match="second backward"):
+        loss.backward()
