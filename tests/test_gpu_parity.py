@@ -485,19 +485,23 @@ def test_gpt_oss_head_256k_sequence_workload_sampled():
 
 
 # ------------------------------------------------------------------ limits of the supported shapes
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [
     (1, 64, 500, 20, 0),        # one position
     (40, 8, 3000, 2048, 0),     # the largest K, and the smallest d
-    (33, 16, 2048, 2048, 16),   # K = V at the largest K
+    (33, 16, 2048, 2048, 16),   # K = V at the largest K: every id of every slice cached
 ])
-def test_shape_limits(shape):
+def test_shape_limits(shape, dtype):
     binding = _need_gpu()
     N, d, V, K, chunk = shape
-    say(f"[case] shape limit N={N} d={d} V={V} K={K} chunk={chunk}")
-    inp = WL.small(N, d, V, K, dtype="f32", seed=N * 7 + K)
-    g = run_gpu(binding, inp, "f32", chunk=chunk, rows=True)
+    say(f"[case] shape limit {dtype} N={N} d={d} V={V} K={K} chunk={chunk}")
+    inp = WL.small(N, d, V, K, dtype=dtype, seed=N * 7 + K)
+    g = run_gpu(binding, inp, dtype, chunk=chunk, rows=True)
     o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], want_rows=True)
-    check(g, o, "f32", f"limit {shape}")
+    check(g, o, dtype, f"limit {dtype} {shape}")
+    # the logits at the cached ids are the contraction's own: the KL per row
+    # is fp32-accurate even on the bf16 path
+    np.testing.assert_allclose(g["kl"], o["kl"], rtol=2e-5 if dtype == "f32" else 1e-4, atol=1e-5)
 
 
 def test_single_valid_position():
