@@ -416,9 +416,19 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       CKL_TRY(launch_id_tables(ids_c, (int)K, rows, V, live, base + L.bits_off, base + L.pre_off, L.cpad,
                                (int32_t*)(base + L.rank_off), err, stream));
     }
+    // The recomputing backward knows the log-normalisers before the logits:
+    // their epilogue stores the gradient's dense part, and no dense pass runs.
+    GradTerms gt{};
+    if (pass == PASS_BWD) {
+      gt.lse = lse_in + r0;
+      gt.rowmap = live ? vidx : nullptr;
+      gt.scale = (const float*)((const char*)scal + kScaleOffset);
+      gt.gscale = gscale;
+    }
     {
       Timed t(T_LOGITS, stream, tm);
-      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, &tab, live, stream));
+      CKL_TRY(launch_logits(dt, Wt, Hc, V, d, rows, P, L.pblk, part, L.n_slices, &tab,
+                            pass == PASS_BWD ? &gt : nullptr, live, stream));
     }
     {
       RowArgs a{};
@@ -445,7 +455,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
       Timed t(T_ROWS, stream, tm);
       CKL_TRY(launch_row_stats(dt, a, stream));
       if (want_grad) {
-        CKL_TRY(launch_dense(dt, a, stream));
+        if (pass != PASS_BWD) CKL_TRY(launch_dense(dt, a, stream));
         CKL_TRY(launch_scatter(dt, a, stream));
       }
     }

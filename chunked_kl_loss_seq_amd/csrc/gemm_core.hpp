@@ -112,6 +112,16 @@ struct GemmParams {
   int64_t id_cpad;
   float* zs;
   int zk;
+  // EPI_LOGITS, or null: the rows' log-normalisers are already known (the
+  // recomputing backward), so the epilogue stores the gradient's dense part
+  // G = f p, f = w exp(mx - lse), itself, with the same fp32 operations as the
+  // separate dense pass: lse of row n is g_lse[g_rowmap ? g_rowmap[n] : n];
+  // w = *g_scale (times *g_gscale if not null) for rows below valid_n (and
+  // *live), 0 for the others; ids at or past valid_m get 0.
+  const float* g_lse;
+  const int* g_rowmap;
+  const float* g_scale;
+  const float* g_gscale;
 };
 
 // ---------------------------------------------------------------- LDS layouts
@@ -445,6 +455,22 @@ __device__ inline float pick16(const f32x16& v, int r) {
   return (r & 8) ? hi : lo;
 }
 
+// Gradient weight of the recomputing backward (EPI_LOGITS with g_lse): w and
+// the compacted chunk's row count (all rows when not compacted).
+__device__ inline void grad_weight(const GemmParams& p, float& w, int& live) {
+  w = p.g_gscale != nullptr ? *p.g_scale * *p.g_gscale : *p.g_scale;
+  live = p.live != nullptr ? __builtin_amdgcn_readfirstlane(*p.live) : 0x7FFFFFFF;
+}
+// Whether token n is a row of the chunk (of its compacted rows): rows past it
+// hold no exp values, possibly not even numbers, and are stored as zeros.
+__device__ inline bool grad_row(const GemmParams& p, int64_t n, int live) { return n < p.valid_n && n < live; }
+// f = w exp(mx - lse) of row n's slice: the factor the dense pass would apply.
+__device__ inline float grad_factor(const GemmParams& p, int64_t n, float mx, float w, int live) {
+  if (!grad_row(p, n, live)) return 0.f;
+  const float lse = p.g_lse[p.g_rowmap != nullptr ? p.g_rowmap[n] : n];
+  return w * __expf(mx - lse);
+}
+
 // LDS bytes after the stage ring for the tile's id tables: 256 tokens x 2
 // slices x 16-byte masks, then 256 tokens x (count below slice s0, count below
 // slice s0 + 1) as two uint16.
@@ -682,6 +708,10 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     // read before the first is needed (one LDS round trip)
     u32x4 idw[FN];
     uint32_t idpre[FN];
+    float gf[FN];
+    float gw = 0.f;
+    int glive = 0x7FFFFFFF;
+    if (p.g_lse != nullptr) grad_weight(p, gw, glive);
     if (p.id_bits != nullptr) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -753,10 +783,29 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
       sum += __shfl_xor(sum, 16);
       sum += __shfl_xor(sum, 32);
       if (g == 0 && n < p.valid_n && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, sum);
+      if (p.g_lse != nullptr) {
+        gf[j] = grad_factor(p, n, mx, gw, glive);
+        if (!grad_row(p, n, glive)) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;  // f = 0 then stores zeros
+        }
+      }
     }
-    // The exp values leave through this wave's 16 KiB of LDS in the tiles' own
-    // order (token row t of tile i / 4, 16-byte chunks XOR-swizzled by the
-    // row) as 16 coalesced 1 KiB stores, as in the 32-wide epilogue.
+    // The exp values (or, with g_lse, the gradient values) leave through this
+    // wave's 16 KiB of LDS in the tiles' own order (token row t of tile i / 4,
+    // 16-byte chunks XOR-swizzled by the row) as 16 coalesced 1 KiB stores, as
+    // in the 32-wide epilogue.
+    if (p.g_lse != nullptr) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = (mfull || m0lane + 16 * i + r < vm) ? gf[j] * (float)(__bf16)acc[i][j][r] : 0.f;
+    }
     __syncthreads();
     char* wl = smem + wave * 16384;
 #pragma unroll
@@ -798,6 +847,9 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
     const int vm = (int)(p.valid_m < (int64_t)0x7FFFFFFF ? p.valid_m : (int64_t)0x7FFFFFFF);
     u32x4 idw[FN];
     uint32_t idpre[FN];
+    float gw = 0.f;
+    int glive = 0x7FFFFFFF;
+    if (p.g_lse != nullptr) grad_weight(p, gw, glive);
     if (p.id_bits != nullptr) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
@@ -872,6 +924,19 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
       sum += __shfl_xor(sum, 32);
       const bool nvalid = n < p.valid_n;
       if (h == 0 && nvalid && slice < p.n_slices) p.part[n * p.n_slices + slice] = make_float2(mx, sum);
+      if (p.g_lse != nullptr) {
+        // the gradient's dense part instead of the exp values (zero past V
+        // and past the rows)
+        const float f = grad_factor(p, n, mx, gw, glive);
+        const bool rok = grad_row(p, n, glive);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = m0lane + i * 32 + (r >> 2) * 8 + (r & 3) < vm;
+            acc[i][j][r] = (rok && (mfull || ok)) ? f * (float)(T)acc[i][j][r] : 0.f;
+          }
+      }
       if constexpr (sizeof(T) == 2) continue;  // bf16: stored through LDS below
       if (nvalid) {
         // tile row of token n; the 4 values of (i, q) are consecutive ids

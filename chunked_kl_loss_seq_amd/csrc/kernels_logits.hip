@@ -8,8 +8,8 @@
 namespace ckl {
 
 hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, const IdTables* tab, const int* live,
-                         hipStream_t s) {
+                         int64_t pblk, float2* part, int n_slices, const IdTables* tab, const GradTerms* grad,
+                         const int* live, hipStream_t s) {
   GemmParams p{};
   p.live = live;
   p.a = Operand{Wt, 0, V, d, tile_row_stride(d)};  // tiled: storage row = vocabulary id, column = d
@@ -27,6 +27,12 @@ hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, in
   p.valid_n = rows;
   p.part = part;
   p.n_slices = n_slices;
+  if (grad != nullptr) {
+    p.g_lse = grad->lse;
+    p.g_rowmap = grad->rowmap;
+    p.g_scale = grad->scale;
+    p.g_gscale = grad->gscale;
+  }
   if (tab != nullptr) {
     p.id_bits = tab->bits;
     p.id_pre = tab->pre;

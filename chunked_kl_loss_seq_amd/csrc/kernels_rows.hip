@@ -57,6 +57,7 @@ struct Scalars {
   unsigned err;  // at kErrOffset: flags of launch_id_tables, cleared by the valid count
 };
 static_assert(offsetof(Scalars, err) == kErrOffset, "error flags offset");
+static_assert(offsetof(Scalars, scale) == kScaleOffset, "gradient weight offset");
 
 // Element (row r, column v) of a 64 x 64-tiled matrix whose tile rows are
 // `blk` elements apart.

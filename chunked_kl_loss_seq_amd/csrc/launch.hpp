@@ -42,15 +42,26 @@ inline int64_t id_table_pairs(int64_t V) { return (V + 255) / 256; }
 hipError_t launch_id_tables(const int32_t* ids, int K, int64_t rows, int64_t V, const int* live, void* bits,
                             void* pre, int64_t cpad, int32_t* rank, unsigned* err, hipStream_t s);
 
+// The recomputing backward knows each row's log-normaliser before its logits:
+// the logits epilogue then stores the gradient's dense part itself.
+struct GradTerms {
+  const float* lse;     // [rows] log-normalisers of the chunk's rows
+  const int* rowmap;    // compacted chunk: chunk row of each compacted row (lse index), or null
+  const float* scale;   // device scalar 1 / n_valid
+  const float* gscale;  // device scalar multiplying the gradient, or null
+};
+
 // Logits of one chunk, kept as exp values: per (row n < rows, 128-id slice s)
 // the slice max m and sum of exp(z - m) into part[n][s], and exp(z - m) for
 // every z = H_c[n] . W[v] into P (element type of dt, tiled, tile rows pblk
 // elements apart).  With tab, the fp32 logit at every cached id also goes to
-// tab->zs.
+// tab->zs.  With grad, P receives w exp(m - lse) exp(z - m) instead, exactly
+// as launch_dense would leave it (w = scale (x gscale) for the rows, 0 past
+// them and past V).
 // W is the tiled copy of the weight (tile_row_stride(d) elements between tile rows).
 hipError_t launch_logits(Dtype dt, const void* Wt, const void* Hc, int64_t V, int64_t d, int64_t rows, void* P,
-                         int64_t pblk, float2* part, int n_slices, const IdTables* tab, const int* live,
-                         hipStream_t s);
+                         int64_t pblk, float2* part, int n_slices, const IdTables* tab, const GradTerms* grad,
+                         const int* live, hipStream_t s);
 
 // dH partial slabs of one chunk: slab[s][n][j] = sum over the s-th vocabulary
 // split of G[n][v] W[v][j].  G is tiled like P, tile rows gblk elements apart;
@@ -133,8 +144,10 @@ hipError_t launch_untile(Dtype g_dt, const void* P, int64_t pblk, int64_t rows, 
 hipError_t launch_finalize(const float* kl, int64_t N, const void* scal, float* out_loss, hipStream_t s);
 
 constexpr int kMaxK = 2048;
-// byte offset, in the device scalar block, of the input-check flags (bit 0: a
-// cached id outside [0, V); bit 1: an id repeated within a row)
+// byte offsets, in the device scalar block, of the gradient weight 1 / n_valid
+// (fp32) and of the input-check flags (bit 0: a cached id outside [0, V);
+// bit 1: an id repeated within a row)
+constexpr int kScaleOffset = 8;
 constexpr int kErrOffset = 16;
 
 }  // namespace ckl

@@ -52,8 +52,10 @@ def to_dev(inp, dtype):
             torch.from_numpy(inp["mask"]).to(dev).contiguous())
 
 
-def fused_and_two_pass(binding, inp, dtype, chunk, fwd_chunk=None):
+def fused_and_two_pass(binding, inp, dtype, chunk, fwd_chunk=None, masked=True):
     H, W, ids, T, mask = to_dev(inp, dtype)
+    if not masked:
+        mask = None
     N = H.shape[0]
     kl_f = torch.empty(N, dtype=torch.float32, device=H.device)
     lse_f = torch.empty_like(kl_f)
@@ -84,6 +86,34 @@ def test_two_pass_bitwise_equals_fused(dtype, shape):
     say(f"[case] two-pass vs fused {dtype} N={N} d={d} V={V} K={K} chunk={chunk}")
     inp = WL.small(N, d, V, K, dtype=dtype, mask="random5", seed=3 * N + d)
     assert_bitwise(*fused_and_two_pass(binding, inp, dtype, chunk))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_two_pass_bitwise_equals_fused_without_mask(dtype):
+    # every row counts: the chunks are not compacted, so the backward's
+    # gradient epilogue indexes the saved log-normaliser by chunk row directly
+    binding = _need_gpu()
+    N, d, V, K, chunk = 700, 256, 2111, 64, 320
+    say(f"[case] two-pass vs fused, no mask, {dtype} N={N} d={d} V={V} K={K} chunk={chunk}")
+    inp = WL.small(N, d, V, K, dtype=dtype, mask="random5", seed=23)
+    assert_bitwise(*fused_and_two_pass(binding, inp, dtype, chunk, masked=False))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_two_pass_unit_upstream_gradient_is_bitwise_neutral(dtype):
+    # w = (1 / n_valid) x 1.0 is the same fp32 number as 1 / n_valid, so an
+    # upstream gradient of exactly 1 read from the device changes no bit
+    binding = _need_gpu()
+    N, d, V, K, chunk = 500, 192, 1500, 40, 256
+    say(f"[case] two-pass grad_loss = 1 vs none {dtype} N={N} d={d} V={V} K={K}")
+    inp = WL.small(N, d, V, K, dtype=dtype, mask="random5", seed=29)
+    H, W, ids, T, mask = to_dev(inp, dtype)
+    _, lse = binding.fwd(H, W, ids, T, mask, chunk=chunk)
+    dH_a, dW_a = binding.bwd(H, W, ids, T, lse, mask, chunk=chunk)
+    one = torch.ones((), dtype=torch.float32, device=H.device)
+    dH_b, dW_b = binding.bwd(H, W, ids, T, lse, mask, grad_loss=one, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(dH_a, dH_b) and torch.equal(dW_a, dW_b)
 
 
 def test_forward_is_chunk_invariant_bitwise():
