@@ -65,8 +65,8 @@ Layout make_layout(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_
   uint64_t off = 0;
   L.w_off = off;  // tiled copy of W
   off += align256((uint64_t)((V + 63) / 64) * tile_row_stride(d) * esz);
-  L.p_off = off;
-  off += align256((uint64_t)tile_rows * L.pblk * esz);
+  L.p_off = off;  // the forward alone keeps no exp values
+  if (pass != PASS_FWD) off += align256((uint64_t)tile_rows * L.pblk * esz);
   L.part_off = off;
   off += align256((uint64_t)C * L.n_slices * 8);
   L.scat_off = off;
@@ -366,7 +366,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
                         (long long)V, (long long)K, (long long)L.C, mask ? " masked" : "", fixed_ws ? " noalloc" : "");
   char* base = (char*)ws;
   void* Wt = base + L.w_off;
-  void* P = base + L.p_off;
+  void* P = pass == PASS_FWD ? nullptr : base + L.p_off;
   float2* part = (float2*)(base + L.part_off);
   float* scat = (float*)(base + L.scat_off);
   float* slab = (float*)(base + L.slab_off);

@@ -806,6 +806,7 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
           for (int r = 0; r < 4; ++r)
             acc[i][j][r] = (mfull || m0lane + 16 * i + r < vm) ? gf[j] * (float)(__bf16)acc[i][j][r] : 0.f;
     }
+    if (p.out == nullptr) return;  // forward only: the exp values are not kept
     __syncthreads();
     char* wl = smem + wave * 16384;
 #pragma unroll
@@ -938,7 +939,7 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
           }
       }
       if constexpr (sizeof(T) == 2) continue;  // bf16: stored through LDS below
-      if (nvalid) {
+      if (nvalid && p.out != nullptr) {
         // tile row of token n; the 4 values of (i, q) are consecutive ids
         T* prow = pout + (n >> 6) * p.ldo + (n & 63) * 64;
 #pragma unroll
@@ -970,6 +971,7 @@ __global__ void __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_e
       // the tiles' own order, 16-byte chunks of a token row XOR-swizzled by
       // the row, and leave as 16 fully coalesced 1 KiB stores.
       static_assert(WTM == 128 && WTN == 64 && NW * 16384 <= NS * STAGE, "one wave = two 64 x 64 tiles");
+      if (p.out == nullptr) return;  // forward only: the exp values are not kept
       __syncthreads();
       char* wl = smem + wave * 16384;
 #pragma unroll

@@ -55,7 +55,8 @@ struct GradTerms {
 // the slice max m and sum of exp(z - m) into part[n][s], and exp(z - m) for
 // every z = H_c[n] . W[v] into P (element type of dt, tiled, tile rows pblk
 // elements apart).  With tab, the fp32 logit at every cached id also goes to
-// tab->zs.  With grad, P receives w exp(m - lse) exp(z - m) instead, exactly
+// tab->zs.  P may be null (the forward alone): no exp values are stored.
+// With grad, P receives w exp(m - lse) exp(z - m) instead, exactly
 // as launch_dense would leave it (w = scale (x gscale) for the rows, 0 past
 // them and past V).
 // W is the tiled copy of the weight (tile_row_stride(d) elements between tile rows).

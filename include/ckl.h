@@ -158,7 +158,9 @@ int ckl_fwd_bwd_noalloc(int dtype, const void* H, const void* W, const int32_t* 
  *                                    (0 for masked positions)
  *   row_kl     fp32 [N] or NULL      KL_r (0 for masked positions)
  * With the same inputs and chunk, loss, row_lse and row_kl are bitwise equal
- * to those of ckl_fwd_bwd_ex. */
+ * to those of ckl_fwd_bwd_ex (and they do not depend on the chunk).  No exp
+ * values are kept, so the workspace per row is a small fraction of the fused
+ * call's and the planner's chunk is correspondingly longer. */
 int ckl_fwd(int dtype, const void* H, const void* W, const int32_t* topk_idx, const float* topk_logit,
             const uint8_t* mask, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, float* out_loss,
             float* row_lse, float* row_kl, hipStream_t stream);

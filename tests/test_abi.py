@@ -35,7 +35,7 @@ def test_strerror():
 GiB = 1 << 30
 
 
-def ws_formula(N, d, V, K, C, splits, esz=2):
+def ws_formula(N, d, V, K, C, splits, esz=2, keep_exp=True):
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     pblk = -(-V // 64) * 4096          # elements between 64-row tile rows of the exp / gradient tiles
     tile_rows = -(-C // 64)
@@ -44,7 +44,8 @@ def ws_formula(N, d, V, K, C, splits, esz=2):
     compact = a(C * d * esz) + 2 * a(C * K * 4) + 2 * a(C * 4)  # masked calls: the compacted chunk
     cpad, pairs = -(-C // 256) * 256, -(-V // 256)
     idtab = a(pairs * cpad * 32) + a(pairs * cpad * 4) + 2 * a(C * K * 4)  # cached-id masks, counts, ranks, logits
-    return (a(wt * esz) + a(tile_rows * pblk * esz) + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
+    exp_vals = a(tile_rows * pblk * esz) if keep_exp else 0  # the forward alone keeps none
+    return (a(wt * esz) + exp_vals + a(C * nsl * 8) + a(C * K * 4) + a(splits * C * d * 4)
             + 2 * a(N * 4) + 256 + compact + idtab)
 
 
@@ -139,18 +140,19 @@ def test_timing_query_argument_check():
 
 def test_plan_per_pass():
     # the backward needs the same workspace as the fused call; the forward
-    # alone has no dH split-K slabs, so at equal chunk it is exactly that much
-    # smaller, and the planner can give it longer chunks
+    # alone keeps neither exp values nor dH split-K slabs, so at equal chunk it
+    # is exactly that much smaller, and one chunk covers the 32K-token head
     for (N, d, V, K, C) in [(4096, 2048, 32000, 100, 1024), (600, 200, 1003, 37, 256)]:
         cf, wf = B.plan(N, d, V, K, chunk=C)
         cb, wb = B.plan(N, d, V, K, chunk=C, pass_="bwd")
         c1, w1 = B.plan(N, d, V, K, chunk=C, pass_="fwd")
         assert cf == cb == c1 == min(C, N)
         assert wb == wf
-        assert w1 == ws_formula(N, d, V, K, c1, 0)
+        assert w1 == ws_formula(N, d, V, K, c1, 0, keep_exp=False)
     c_fused, _ = B.plan(32768, 2880, 201088, 100)
     c_fwd, w_fwd = B.plan(32768, 2880, 201088, 100, pass_="fwd")
-    assert w_fwd <= 6 * GiB and c_fwd >= c_fused
+    assert c_fwd == 32768 and w_fwd == ws_formula(32768, 2880, 201088, 100, c_fwd, 0, keep_exp=False)
+    assert w_fwd <= 6 * GiB and c_fwd > c_fused
     L = B.lib()
     c = ctypes.c_int64(0)
     b = ctypes.c_uint64(0)
