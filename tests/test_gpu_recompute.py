@@ -228,6 +228,33 @@ def test_two_pass_gpt_oss_head_planner_chunks_bitwise():
     assert_bitwise(*fused_and_two_pass(binding, inp, "bf16", chunk=0, fwd_chunk=0))
 
 
+def test_forward_on_the_256k_sequence_at_its_planner_chunk_bitwise():
+    # N = 262,144: the forward alone plans 87,552-row chunks, whose cached-id
+    # masks (786 vocabulary pairs x 87,552 rows x 32 B) pass 2 GiB; its loss,
+    # log-normalisers and KL must still be bitwise the fused call's
+    binding = _need_gpu()
+    wl = WL.WORKLOADS[6]
+    c_fused, _ = binding.plan(wl.N, wl.d, wl.V, wl.K)
+    c_fwd, ws_fwd = binding.plan(wl.N, wl.d, wl.V, wl.K, pass_="fwd")
+    pairs = -(-wl.V // 256)
+    assert pairs * (-(-c_fwd // 256) * 256) * 32 > 2**31 and c_fwd > c_fused
+    say(f"[case] forward at its planner chunk, {wl.name}: fwd chunk {c_fwd} ({ws_fwd / 2**30:.2f} GiB), "
+        f"fused chunk {c_fused}; generating inputs")
+    inp = WL.make(6)
+    H, W, ids, T, mask = to_dev(inp, "bf16")
+    kl_f = torch.empty(wl.N, dtype=torch.float32, device=H.device)
+    lse_f = torch.empty_like(kl_f)
+    say(f"[case] forward at its planner chunk, {wl.name}: fused call")
+    loss_f, dH, dW = binding.fwd_bwd(H, W, ids, T, mask, row_kl=kl_f, row_lse=lse_f)
+    del dH, dW
+    kl_1 = torch.empty_like(kl_f)
+    say(f"[case] forward at its planner chunk, {wl.name}: forward call")
+    loss_1, lse_1 = binding.fwd(H, W, ids, T, mask, row_kl=kl_1)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_1, loss_f), (loss_1.item(), loss_f.item())
+    assert torch.equal(lse_1, lse_f) and torch.equal(kl_1, kl_f)
+
+
 def test_fused_wrapper_scales_in_place_and_refuses_a_second_backward():
     # the fused wrapper's gradients were computed in the forward call; its
     # backward scales them in place by the upstream gradient, once
