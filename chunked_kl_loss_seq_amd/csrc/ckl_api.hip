@@ -462,7 +462,7 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
     if (!want_grad) continue;
     int splits = dh_splits(dt, rows, d, V);
     const int64_t cap = (int64_t)L.splits * L.C / rows;  // slab capacity in splits of this chunk
-    if (splits > cap) splits = (int)cap;
+    if (splits > cap) splits = dh_fit_splits(dt, V, (int)cap);
     {
       Timed t(T_DH, stream, tm);
       CKL_TRY(launch_dh(dt, P, L.pblk, Wt, V, d, rows, slab, splits, live, stream));

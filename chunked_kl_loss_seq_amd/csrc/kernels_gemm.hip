@@ -16,14 +16,19 @@ int d_tile(Dtype dt, int64_t d) {
 }
 
 int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
-  // Pick the k-split count (1..8) that best fills whole waves of 256
-  // workgroups; each split keeps at least 16 k-steps.
+  // Pick the k-split count that best fills whole waves of 256 workgroups:
+  // 1..8, or up to 32 when 8 splits do not fill one wave (small chunks, whose
+  // slabs are small).  Each split keeps at least 8 k-steps, and only counts
+  // that cut the k-steps into exactly that many runs are taken.
   const int64_t tiles = ((rows + 255) / 256) * ((d + d_tile(dt, d) - 1) / d_tile(dt, d));
-  const int64_t ksteps = (V + 63) / 64;
+  const int64_t ksteps = (V + (dt == DT_BF16 ? 63 : 31)) / (dt == DT_BF16 ? 64 : 32);
+  const int max_s = tiles * 8 < 256 ? 32 : 8;
   int best = 1;
   double best_eff = -1.0;
-  for (int s = 1; s <= 8; ++s) {
-    if (s > 1 && ksteps / s < 16) break;
+  for (int s = 1; s <= max_s; ++s) {
+    if (s > 1 && ksteps / s < 8) break;
+    const int64_t per = (ksteps + s - 1) / s;
+    if ((ksteps + per - 1) / per != s) continue;
     const double waves = (double)tiles * s / 256.0;
     const double eff = waves / (double)((int64_t)(waves + 0.999999));
     if (eff > best_eff + 0.02) {
@@ -32,6 +37,13 @@ int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
     }
   }
   return best;
+}
+
+int dh_fit_splits(Dtype dt, int64_t V, int s) {
+  const int64_t ksteps = (V + (dt == DT_BF16 ? 63 : 31)) / (dt == DT_BF16 ? 64 : 32);
+  if (s < 1) return 1;
+  const int64_t per = (ksteps + s - 1) / s;
+  return (int)((ksteps + per - 1) / per);  // at most s, and cuts the k-steps into exactly that many runs
 }
 
 hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int64_t V, int64_t d, int64_t rows,

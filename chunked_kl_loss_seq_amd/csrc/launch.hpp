@@ -79,6 +79,9 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int6
 
 // k-splits used for the dH contraction of a chunk of `rows` rows.
 int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V);
+// The largest split count <= s that cuts the dH k-steps into exactly that many
+// runs (what launch_dh requires).
+int dh_fit_splits(Dtype dt, int64_t V, int s);
 // tile width used along d by the dH and dW contractions.
 int d_tile(Dtype dt, int64_t d);
 
