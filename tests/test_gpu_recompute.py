@@ -116,6 +116,36 @@ def test_two_pass_unit_upstream_gradient_is_bitwise_neutral(dtype):
     assert torch.equal(dH_a, dH_b) and torch.equal(dW_a, dW_b)
 
 
+def _random_cases(n_cases, seed):
+    rng = np.random.default_rng(seed)
+    cases = [(1, 8, 1, 1, 0, "f32", "none"), (1, 64, 300, 7, 0, "bf16", "random5"),
+             (257, 8, 129, 129, 64, "bf16", "none")]
+    while len(cases) < n_cases:
+        N = int(rng.integers(1, 900))
+        d = 8 * int(rng.integers(1, 65))
+        V = int(rng.integers(1, 5000))
+        K = int(rng.integers(1, min(V, 160) + 1))
+        chunk = 0 if rng.random() < 0.4 else int(rng.integers(1, N + 64))
+        dtype = "bf16" if rng.random() < 0.6 else "f32"
+        mask = "random5" if rng.random() < 0.5 else "none"
+        cases.append((N, d, V, K, chunk, dtype, mask))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(16, 2024), ids=lambda c: "x".join(map(str, c)))
+def test_two_pass_bitwise_equals_fused_random_shapes(case):
+    # seeded random small shapes and edge sizes (one row, one id, V below one
+    # slice, K past a 64-id lane group), both element types, with and without
+    # a mask, at the planner's chunk (the forward then plans its own) or a
+    # given one
+    binding = _need_gpu()
+    N, d, V, K, chunk, dtype, mask = case
+    say(f"[case] two-pass vs fused random shape N={N} d={d} V={V} K={K} chunk={chunk} {dtype} mask={mask}")
+    inp = WL.small(N, d, V, K, dtype=dtype, mask="random5" if mask != "none" else "none", seed=N * 7 + V)
+    assert_bitwise(*fused_and_two_pass(binding, inp, dtype, chunk, fwd_chunk=0 if chunk == 0 else None,
+                                       masked=mask != "none"))
+
+
 def test_forward_is_chunk_invariant_bitwise():
     # per-row logits, their slice statistics and the loss's fixed-order sum do
     # not depend on the chunking, so a forward with other chunks gives the
