@@ -331,8 +331,9 @@ bool debug_checks() {
 
 // One call of any pass.  Inputs common to all: H, W, ids, tlogit, mask.
 //   PASS_FUSED: out_loss, dH, dW (+ optional row_kl, row_lse)
-//   PASS_FWD:   out_loss, row_lse (+ optional row_kl)
-//   PASS_BWD:   lse_in (the forward's row_lse), optional gscale; dH, dW
+//   PASS_FWD:   out_loss, row_lse (+ optional row_kl); no exp values are kept
+//   PASS_BWD:   lse_in (the forward's row_lse), optional gscale; dH, dW; the
+//               logits epilogue writes the gradient, so no dense pass runs
 // With fixed_ws set, the call runs in the fixed scratch array of this device
 // (budget kScratchBytes) and allocates nothing: no workspace cache, no timing
 // events.
