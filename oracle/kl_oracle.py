@@ -138,7 +138,7 @@ def kl_dense(H, W, idx, tlogit, mask=None, block=None, want_rows=False):
     H = _f64(H)
     W = _f64(W)
     N = H.shape[0]
-    block = N if not block else int(block)
+    block = max(N, 1) if not block else int(block)  # N = 0: no rows, no blocks
     m, n_valid, scale = _weights(mask, N)
     weight = m * scale
     dH = np.zeros_like(H)

@@ -221,6 +221,19 @@ def test_all_masked_is_zero():
     assert out["loss"] == 0.0 and np.all(out["dH"] == 0) and np.all(out["dW"] == 0)
 
 
+def test_empty_batch_is_an_all_masked_one():
+    # no positions at all: the same reading as no valid position (loss 0, no
+    # gradient), whatever the block size
+    rng = np.random.default_rng(11)
+    H, W, ids, T, _ = rand_problem(rng, 5, 4, 10, 3)
+    masked = O.kl_dense(H, W, ids, T, np.zeros(5, dtype=np.uint8), want_rows=True)
+    for block in (None, 1, 4):
+        out = O.kl_dense(H[:0], W, ids[:0], T[:0], np.zeros(0, dtype=np.uint8), block=block, want_rows=True)
+        assert out["loss"] == masked["loss"] == 0.0 and out["n_valid"] == 0
+        assert out["dH"].shape == (0, 4) and out["kl"].shape == (0,) and out["lse"].shape == (0,)
+        assert np.array_equal(out["dW"], masked["dW"])
+
+
 # ---------------------------------------------------------------- P10 exact gather
 def test_gather_is_exact_copy_with_one_hot_rows():
     rng = np.random.default_rng(12)
