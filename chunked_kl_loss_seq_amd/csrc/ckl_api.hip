@@ -119,10 +119,14 @@ uint64_t budget_from_env(uint64_t b) {
 
 int plan_impl(Pass pass, int64_t N, int64_t d, int64_t V, int64_t K, int64_t chunk, uint64_t budget, size_t esz,
               Layout* out) {
-  if (N <= 0 || d <= 0 || V <= 0 || K <= 0 || chunk < 0) return CKL_EINVAL;
+  if (N < 0 || d <= 0 || V <= 0 || K <= 0 || chunk < 0) return CKL_EINVAL;
   if (K > V) return CKL_EINVAL;
   if (d % 8 != 0 || K > kMaxK) return CKL_EUNSUPPORTED;
   if (V > (int64_t)1 << 26 || N > (int64_t)1 << 31 || d > (int64_t)1 << 20) return CKL_EUNSUPPORTED;
+  if (N == 0) {  // an empty batch: no chunk, no workspace
+    *out = Layout{};
+    return CKL_OK;
+  }
   budget = budget_from_env(budget);
   if (chunk > 0) {
     const int64_t C = chunk < N ? chunk : N;
@@ -342,6 +346,18 @@ int run_impl(Pass pass, Dtype dt, const void* H, const void* W, const int32_t* i
              int64_t K, int64_t chunk, float* out_loss, void* dH, float* dW, float* row_kl, float* row_lse,
              hipStream_t stream, bool fixed_ws = false) {
   const bool want_loss = pass != PASS_BWD, want_grad = pass != PASS_FWD;
+  if (N == 0) {
+    // An empty batch reads no row (its row arrays may be null) and has no
+    // valid position: the loss is 0 and dW is 0.
+    if (!W || (want_loss && !out_loss) || (want_grad && !dW)) return CKL_EINVAL;
+    if (!aligned(W, 16) || !aligned(dW, 16) || !aligned(out_loss, 4)) return CKL_EINVAL;
+    Layout L;
+    const int st = plan_impl(pass, 0, d, V, K, chunk, 0, dt == DT_BF16 ? 2 : 4, &L);
+    if (st != CKL_OK) return st;
+    if (want_loss) CKL_TRY(launch_fill_f32(out_loss, 1, 0.f, stream));
+    if (want_grad) CKL_TRY(launch_fill_f32(dW, V * d, 0.f, stream));
+    return CKL_OK;
+  }
   if (!H || !W || !ids || !tlogit) return CKL_EINVAL;
   if (want_loss && !out_loss) return CKL_EINVAL;
   if (want_grad && (!dH || !dW)) return CKL_EINVAL;
@@ -576,9 +592,10 @@ int ckl_topk(int dtype, const void* logits, int64_t N, int64_t V, int64_t K, int
              hipStream_t stream) {
   if (!dtype_ok(dtype)) return CKL_EINVAL;
   const size_t esz = dtype == CKL_DTYPE_BF16 ? 2 : 4;
+  if (N < 0 || V <= 0 || K <= 0 || K > V) return CKL_EINVAL;
+  if (N == 0) return K > kMaxK ? CKL_EUNSUPPORTED : CKL_OK;  // no rows: nothing to write
   if (!logits || !ids_out || !vals_out) return CKL_EINVAL;
   if (!aligned(logits, esz) || !aligned(ids_out, 4) || !aligned(vals_out, 4)) return CKL_EINVAL;
-  if (N <= 0 || V <= 0 || K <= 0 || K > V) return CKL_EINVAL;
   if (K > kMaxK || V > 0x7FFFFFFFll || N > (int64_t)(0xFFFFFFFFull / 512)) return CKL_EUNSUPPORTED;
   try {
     Timed t(T_TOPK, stream);

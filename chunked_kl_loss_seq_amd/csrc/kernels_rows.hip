@@ -628,6 +628,17 @@ hipError_t launch_zs_from_z(const float* Z, int64_t ldz, const int32_t* ids, con
   return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(256) fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
 hipError_t launch_mask_count(const uint8_t* mask, int64_t N, void* scal, hipStream_t s) {
   hipLaunchKernelGGL(mask_count_kernel, dim3(1), dim3(1024), 0, s, mask, N, (Scalars*)scal);
   return hipGetLastError();

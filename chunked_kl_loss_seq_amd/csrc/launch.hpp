@@ -131,6 +131,8 @@ struct RowArgs {
   int32_t* sid_dbg;     // optional [rows, K]
 };
 hipError_t launch_row_stats(Dtype g_dt, const RowArgs& a, hipStream_t s);
+// p[0 .. n) = v (a kernel, not a memset node, so that the call stays capturable)
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_dense(Dtype g_dt, const RowArgs& a, hipStream_t s);
 hipError_t launch_scatter(Dtype g_dt, const RowArgs& a, hipStream_t s);
 

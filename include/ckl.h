@@ -42,6 +42,10 @@
  *     call returns.  Work is enqueued on `stream` with no host synchronisation,
  *     so inputs and outputs must stay alive until the stream has finished;
  *   - d must be a multiple of 8; 1 <= K <= min(V, 2048);
+ *   - N = 0 is an empty batch: no row is read (H, ids, logits, mask, dH and
+ *     the per-position arrays may be null), and a loss call writes 0 to
+ *     out_loss and zeros to dW, the result for a batch with no valid
+ *     position; ckl_plan gives chunk 0 and 0 bytes, ckl_topk does nothing;
  *   - the library holds one grow-only device workspace per (device, stream),
  *     sized by ckl_plan; ckl_release_workspace frees them all.
  *
@@ -69,7 +73,7 @@ extern "C" {
 
 typedef enum {
   CKL_OK = 0,
-  CKL_EINVAL = -1,       /* null or misaligned pointer, non-positive size, K > V, chunk < 0 */
+  CKL_EINVAL = -1,       /* null or misaligned pointer, N < 0, d, V or K < 1, K > V, chunk < 0 */
   CKL_ENOMEM = -2,       /* device workspace allocation failed */
   CKL_EBUDGET = -3,      /* no chunk size fits the workspace budget (or the given chunk does not) */
   CKL_EHIP = -4,         /* a HIP runtime call failed */

@@ -19,7 +19,7 @@ static int g_fail = 0;
 
 int main() {
   // planner: every plan fits its budget, chunks are within N
-  const int64_t Ns[] = {1, 2, 255, 256, 257, 4096, 32768, 131072, 262144, (int64_t)1 << 31};
+  const int64_t Ns[] = {0, 1, 2, 255, 256, 257, 4096, 32768, 131072, 262144, (int64_t)1 << 31};
   const int64_t ds[] = {8, 256, 2880, 3072, (int64_t)1 << 20};
   const int64_t Vs[] = {1, 127, 128, 129, 32000, 201088, (int64_t)1 << 26};
   const int64_t Ks[] = {1, 100, 2048};
@@ -38,7 +38,9 @@ int main() {
                   uint64_t bytes = 0;
                   const int st = ckl_plan_pass(pass, N, d, V, K, dt, c, b, &C, &bytes);
                   if (K > V) CHECK(st == CKL_EINVAL);
-                  if (st == CKL_OK) {
+                  if (st == CKL_OK && N == 0) {
+                    CHECK(C == 0 && bytes == 0);  // an empty batch: no chunk, no workspace
+                  } else if (st == CKL_OK) {
                     ++planned;
                     CHECK(C >= 1 && C <= N);
                     if (c > 0) CHECK(C == (c < N ? c : N));
@@ -87,6 +89,16 @@ int main() {
   CHECK(ckl_bwd(0, g, g, ids, tl, nullptr, nullptr, nullptr, 4, 8, 10, 2, 0, g, fo, nullptr) == CKL_EINVAL);
   CHECK(ckl_bwd(0, g, g, ids, tl, nullptr, fo, (const float*)mis, 4, 8, 10, 2, 0, g, fo, nullptr) == CKL_EINVAL);
   CHECK(ckl_topk(0, nullptr, 4, 10, 2, (int32_t*)g, fo, nullptr) == CKL_EINVAL);
+  CHECK(ckl_topk(0, nullptr, 0, 10, 2, nullptr, nullptr, nullptr) == CKL_OK);  // no rows: nothing to do
+  CHECK(ckl_topk(0, g, -1, 10, 2, (int32_t*)g, fo, nullptr) == CKL_EINVAL);
+  // an empty batch still needs W and the outputs it writes
+  CHECK(ckl_fwd_bwd(nullptr, g, nullptr, nullptr, nullptr, 0, 8, 10, 2, 0, fo, nullptr, nullptr, nullptr) ==
+        CKL_EINVAL);
+  CHECK(ckl_fwd_bwd(nullptr, g, nullptr, nullptr, nullptr, 0, 8, 10, 11, 0, fo, nullptr, fo, nullptr) == CKL_EINVAL);
+  CHECK(ckl_fwd(0, nullptr, g, nullptr, nullptr, nullptr, 0, 8, 10, 2, 0, nullptr, nullptr, nullptr, nullptr) ==
+        CKL_EINVAL);
+  CHECK(ckl_bwd(0, nullptr, g, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 8, 10, 2, 0, nullptr, nullptr,
+                nullptr) == CKL_EINVAL);
   CHECK(ckl_topk(0, g, 4, 5000, 3000, (int32_t*)g, fo, nullptr) == CKL_EUNSUPPORTED);
   CHECK(ckl_topk(0, g, 4, 10, 11, (int32_t*)g, fo, nullptr) == CKL_EINVAL);
   CHECK(ckl_debug_rows(nullptr, ids, tl, nullptr, 4, 10, 2, 1.f, 1, fo, (int32_t*)g, g, fo, fo, nullptr) ==

@@ -100,13 +100,24 @@ def test_plan_budget_errors():
 
 
 @pytest.mark.parametrize("args,status", [
-    ((0, 8, 10, 1), -1), ((4, 0, 10, 1), -1), ((4, 8, 0, 1), -1), ((4, 8, 10, 0), -1),
+    ((-1, 8, 10, 1), -1), ((4, 0, 10, 1), -1), ((4, 8, 0, 1), -1), ((4, 8, 10, 0), -1),
     ((4, 8, 10, 11), -1), ((4, 12, 10, 2), -5), ((4, 8, 5000, 3000), -5),
 ])
 def test_plan_argument_errors(args, status):
     with pytest.raises(B.CklError) as e:
         B.plan(*args)
     assert e.value.status == status
+
+
+def test_plan_empty_batch():
+    # N = 0: no chunk and no workspace, for every call; the other sizes are
+    # still checked
+    for pass_ in ("fused", "fwd", "bwd"):
+        assert B.plan(0, 2880, 201088, 100, pass_=pass_) == (0, 0)
+    assert B.plan(0, 8, 10, 1, dtype="f32") == (0, 0)
+    with pytest.raises(B.CklError) as e:
+        B.plan(0, 8, 10, 11)
+    assert e.value.status == -1
 
 
 def test_plan_negative_chunk():
@@ -191,7 +202,9 @@ def test_topk_rejects_bad_arguments_before_any_gpu_call():
     assert L.ckl_topk(0, good, 4, 10, 2, z, good, z) == -1          # null ids
     assert L.ckl_topk(1, vp((1 << 20) + 2), 4, 10, 2, good, good, z) == -1  # fp32 logits misaligned
     assert L.ckl_topk(0, good, 4, 10, 11, good, good, z) == -1      # K > V
-    assert L.ckl_topk(0, good, 0, 10, 2, good, good, z) == -1       # N = 0
+    assert L.ckl_topk(0, good, 0, 10, 2, good, good, z) == 0        # N = 0: nothing to do
+    assert L.ckl_topk(0, z, 0, 10, 2, z, z, z) == 0                  # ... with null buffers
+    assert L.ckl_topk(0, good, -1, 10, 2, good, good, z) == -1      # N < 0
     assert L.ckl_topk(0, good, 4, 5000, 3000, good, good, z) == -5  # K > 2048
     assert L.ckl_topk(9, good, 4, 10, 2, good, good, z) == -1       # unknown dtype
 
@@ -242,4 +255,6 @@ def test_plan_signature_budget_then_outputs():
     assert (c.value, b.value) == B.plan(32768, 2880, 201088, 100)
     assert L.ckl_plan(32768, 2880, 201088, 100, 0, 100 << 20, ctypes.byref(c), ctypes.byref(b)) == -3
     assert L.ckl_plan(32768, 2880, 201088, 100, 0, 3 << 30, None, None) == 0
-    assert L.ckl_plan(0, 2880, 201088, 100, 0, 0, None, None) == -1
+    assert L.ckl_plan(0, 2880, 201088, 100, 0, 0, ctypes.byref(c), ctypes.byref(b)) == 0  # empty batch
+    assert (c.value, b.value) == (0, 0)
+    assert L.ckl_plan(-1, 2880, 201088, 100, 0, 0, None, None) == -1

@@ -271,6 +271,40 @@ def test_all_masked_gives_zero():
     assert np.all(g["dH"] == 0) and np.all(g["dW"] == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_batch_gives_zero(dtype):
+    # N = 0: every loss call writes the oracle's no-valid-position result
+    # (loss 0, dW 0) over outputs that held NaN, and reads no row
+    binding = _need_gpu()
+    say(f"[case] empty batch {dtype}")
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d, V, K = 64, 500, 10
+    inp = WL.small(1, d, V, K, dtype=dtype, seed=4)
+    W = torch.from_numpy(inp["W"]).to(dev).to(tdt).contiguous()
+    H = torch.empty((0, d), dtype=tdt, device=dev)
+    ids = torch.empty((0, K), dtype=torch.int32, device=dev)
+    T = torch.empty((0, K), dtype=torch.float32, device=dev)
+    o = O.kl_dense(inp["H"][:0], inp["W"], inp["ids"][:0], inp["tlogit"][:0], inp["mask"][:0])
+    nan = float("nan")
+    for noalloc in (False, True):
+        loss = torch.full((), nan, dtype=torch.float32, device=dev)
+        dW = torch.full((V, d), nan, dtype=torch.float32, device=dev)
+        loss, dH, dW = binding.fwd_bwd(H, W, ids, T, None, out_loss=loss, dW=dW, noalloc=noalloc)
+        torch.cuda.synchronize()
+        assert loss.item() == o["loss"] == 0.0 and dH.shape == (0, d)
+        assert np.array_equal(dW.cpu().numpy(), o["dW"])
+    loss = torch.full((), nan, dtype=torch.float32, device=dev)
+    loss, lse = binding.fwd(H, W, ids, T, torch.empty(0, dtype=torch.uint8, device=dev), out_loss=loss)
+    dW = torch.full((V, d), nan, dtype=torch.float32, device=dev)
+    dH, dW = binding.bwd(H, W, ids, T, lse, dW=dW)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and lse.shape == (0,) and dH.shape == (0, d)
+    assert np.array_equal(dW.cpu().numpy(), o["dW"])
+    ids_k, vals_k = binding.topk(torch.empty((0, V), dtype=tdt, device=dev), K)
+    assert ids_k.shape == (0, K) and vals_k.shape == (0, K)
+
+
 def test_teacher_equals_student_full_vocab_fp32():
     binding = _need_gpu()
     say("[case] K = V, teacher = student")
