@@ -8,11 +8,12 @@ namespace ckl {
 constexpr int kGroupM = 4;
 
 // bf16: 256-wide tiles along d (8 waves of 128 x 64), measured faster than
-// 192-wide ones even where 192 divides d and 256 does not; fp32 (wider
-// fragments, register-bound): 192 where it divides d.
+// 192-wide ones even where 192 divides d and 256 does not.  fp32 fragments are
+// twice as wide: 192 where it divides d (and 256 does not), else 128, whose
+// 64 x 64 wave tiles leave the loop spill-free (256 x 256 spilled).
 int d_tile(Dtype dt, int64_t d) {
   if (dt == DT_BF16) return 256;
-  return (d % 192 == 0 && d % 256 != 0) ? 192 : 256;
+  return (d % 192 == 0 && d % 256 != 0) ? 192 : 128;
 }
 
 int dh_splits(Dtype dt, int64_t rows, int64_t d, int64_t V) {
@@ -68,7 +69,7 @@ hipError_t launch_dh(Dtype dt, const void* G, int64_t gblk, const void* Wt, int6
   if (p.splits != splits) return hipErrorInvalidValue;
   if (dt == DT_BF16) return launch_gemm<__bf16, 256, 256, 2, 4, true, false, EPI_SLAB, 128, 2>(p, s);
   if (bn == 192) return launch_gemm<float, 256, 192, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
-  return launch_gemm<float, 256, 256, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
+  return launch_gemm<float, 256, 128, 4, 2, true, false, EPI_SLAB, 128, 2>(p, s);
 }
 
 hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int64_t V, int64_t d, int64_t rows,
@@ -92,7 +93,7 @@ hipError_t launch_dw(Dtype dt, const void* G, int64_t gblk, const void* Hc, int6
   p.beta = beta;
   if (dt == DT_BF16) return launch_gemm<__bf16, 256, 256, 2, 4, false, false, EPI_ACCUM, 128, 2>(p, s);
   if (bn == 192) return launch_gemm<float, 256, 192, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
-  return launch_gemm<float, 256, 256, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
+  return launch_gemm<float, 256, 128, 4, 2, false, false, EPI_ACCUM, 128, 2>(p, s);
 }
 
 // ---------------------------------------------------------------- tiled copy
