@@ -118,7 +118,20 @@ def traffic_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, commands
             f"write {rec['write_bytes_per_launch'] / 1e9:.2f} GB per launch -> {out}")
 
 
-def cpu_baseline(number, rows):
+def resolve_workload(number, dtype=None):
+    """Named workload ``number``, with H, W and dH in ``dtype`` instead of its own
+    type when given (same shapes, seed and recipe; the name records the change)."""
+    import dataclasses
+
+    from chunked_kl_loss_seq_amd import workloads as WL
+
+    wl = WL.WORKLOADS[number]
+    if dtype and dtype != wl.dtype:
+        wl = dataclasses.replace(wl, dtype=dtype, name=f"{wl.name}-{dtype}")
+    return wl
+
+
+def cpu_baseline(number, rows, wl=None):
     """The oracle as it stands, timed on the host cores over a bounded sample."""
     import numpy as np  # noqa: F401
 
@@ -131,7 +144,8 @@ def cpu_baseline(number, rows):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    inp = WL.make(number, rows=rows)
+    wl = wl or WL.WORKLOADS[number]
+    inp = WL.make_custom(wl, number, rows=rows)
     t0 = time.perf_counter()
     O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"])
     dt = time.perf_counter() - t0
@@ -139,7 +153,7 @@ def cpu_baseline(number, rows):
     n = len(inp["mask"])
     return {"value": valid / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
-            "sample": (f"first {n} positions of the same workload" if n < WL.WORKLOADS[number].N
+            "sample": (f"first {n} positions of the same workload" if n < wl.N
                        else "the whole workload")
             + f", float64 NumPy/BLAS dense definition, {dt:.2f} s wall"}
 
@@ -297,6 +311,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="named workload number (4 = gpt-oss head, 32K tokens)")
     ap.add_argument("--chunk", type=int, default=-1, help="rows per chunk (default: the workload's own)")
+    ap.add_argument("--dtype", choices=["bf16", "f32"], default=None,
+                    help="type of H, W and dH in place of the workload's own (fused and two-pass runs)")
     ap.add_argument("--variant", choices=["fused", "two-pass", "topk"], default="fused",
                     help="fused: one ckl_fwd_bwd call per step; two-pass: ckl_fwd then ckl_bwd (logits recomputed); "
                          "topk: the teacher top-K cache writer (ckl_topk) over --topk-rows rows")
@@ -352,10 +368,10 @@ def main():
         log("no GPU visible")
         sys.exit(1)
     binding.lib()
-    wl = WL.WORKLOADS[args.workload]
+    wl = resolve_workload(args.workload, args.dtype)
     chunk = wl.chunk if args.chunk < 0 else args.chunk
-    log(f"[bench] generating {wl.name}: N={wl.N} d={wl.d} V={wl.V} K={wl.K}")
-    inp = WL.make(args.workload)
+    log(f"[bench] generating {wl.name}: N={wl.N} d={wl.d} V={wl.V} K={wl.K} {wl.dtype}")
+    inp = WL.make_custom(wl, args.workload)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     H = torch.from_numpy(inp["H"]).to(dev).to(tdt)
@@ -436,7 +452,7 @@ def main():
     if not args.no_cpu_baseline:
         rows = args.cpu_rows if args.cpu_rows > 0 else (N if N <= 8192 else 4096)
         log(f"[bench] timing the oracle on {rows} positions")
-        cpu = cpu_baseline(args.workload, rows)
+        cpu = cpu_baseline(args.workload, rows, wl)
         log(f"[bench] oracle {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     metric = "fused KL fwd+bwd tokens/s + MFMA TFLOP/s % peak; peak workspace GiB"

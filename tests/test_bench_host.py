@@ -6,6 +6,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -82,3 +83,21 @@ def test_traffic_kinds_pick_the_three_gemms_apart():
     for kind, name in names.items():
         hits = [k for k, (tags, _) in bench.TRAFFIC_KINDS.items() if all(tg in name for tg in tags)]
         assert hits == [kind]
+
+
+def test_dtype_override_keeps_the_workload_and_renames_it():
+    import bench
+    from chunked_kl_loss_seq_amd import workloads as WL
+
+    wl = bench.resolve_workload(2, "f32")
+    base = WL.WORKLOADS[2]
+    assert (wl.N, wl.d, wl.V, wl.K, wl.chunk, wl.ids, wl.mask) == (base.N, base.d, base.V, base.K, base.chunk,
+                                                                      base.ids, base.mask)
+    assert wl.dtype == "f32" and wl.name == "bf16-32k-vocab-f32" and base.dtype == "bf16"
+    assert bench.resolve_workload(4) is WL.WORKLOADS[4] and bench.resolve_workload(1, "f32") is WL.WORKLOADS[1]
+    # the same seeded draws of H and W, only without the bf16 rounding (the
+    # cached ids, half of them the student's own top-100, follow the inputs)
+    a = WL.make_custom(wl, 2, rows=8)
+    b = WL.make(2, rows=8)
+    assert np.array_equal(WL.round_bf16(a["H"]), b["H"]) and np.array_equal(WL.round_bf16(a["W"]), b["W"])
+    assert a["ids"].shape == b["ids"].shape and not np.array_equal(a["H"], b["H"])
