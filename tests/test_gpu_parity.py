@@ -586,6 +586,24 @@ def test_seeded_random_shapes(case):
 
 # ------------------------------------------------------------------ masked tails
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_row_chunks(dtype):
+    # the finest chunking: 37 chunks of one row (and 13 of three), each a
+    # single partial tile in every contraction, with dH split far along V;
+    # the per-row results equal the one-chunk call's, and all match the oracle
+    binding = _need_gpu()
+    N, d, V, K = 37, 96, 1500, 20
+    say(f"[case] one-row chunks {dtype}")
+    inp = WL.small(N, d, V, K, dtype=dtype, ids="zipf", mask="random5", seed=41)
+    o = O.kl_dense(inp["H"], inp["W"], inp["ids"], inp["tlogit"], inp["mask"], want_rows=True)
+    res = {c: run_gpu(binding, inp, dtype, chunk=c, rows=True) for c in (1, 3, N)}
+    for c, g in res.items():
+        check(g, o, dtype, f"chunk {c}")
+        # KL and log-normaliser per row do not depend on the chunking
+        assert np.array_equal(g["kl"], res[N]["kl"]) and np.array_equal(g["lse"], res[N]["lse"])
+        assert abs(g["loss"] - res[N]["loss"]) <= 1e-6 * abs(res[N]["loss"])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_masked_chunk_tails_are_skipped_and_exact(dtype):
     # right-padded sequences: the rows after each chunk's last valid row are
     # skipped by every kernel (whole logits and dH tiles, dW k-steps); one
